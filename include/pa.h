@@ -1,0 +1,267 @@
+/*
+ * pa.h — paged KV cache and paged decode attention for AMD Instinct MI355X
+ * (gfx950).  The library is libpa.so; this header is its whole public
+ * interface.
+ *
+ * What it computes (pages cited by title and section):
+ *   [P1] "Paged Attention：大模型推理显存优化的核心方案" (learnblockchain.cn)
+ *   [P2] "PagedAttention：操作系统级 KV 缓存虚拟内存管理" (freeguideonline.com)
+ *   [P3] "PagedAttention 和 vLLM" (aiunderstanding.org)
+ *
+ *   - The KV cache is a pool of fixed-size blocks, each holding the K and V of
+ *     block_size tokens; a sequence's blocks are scattered through the pool and
+ *     found through its block table ([P1] "Paged Attention 的工作原理",
+ *     "块表（Block Table）"; [P2] §2.1, §2.3).
+ *   - A decode step appends the new token's K/V into its slot, opening a block
+ *     when the last one is full, then attends over every cached token
+ *     ([P2] §3.2.2).
+ *   - Attention is softmax(q Kᵀ/√d) V ([P2] §1.1), one query row per head.
+ *   - Free blocks live in a pool any request may draw from; finished requests
+ *     return theirs ([P2] §3.3).  Shared blocks are refcounted and read-only;
+ *     a write into one copies it first ([P2] §3.4; [P3] "技术洞察").
+ *
+ * Conventions
+ *   - Every function returns pa_status: PA_OK (0) or a negative error code;
+ *     pa_last_error() gives a message for the calling thread's last failure.
+ *   - Device calls (pa_write_kv, pa_copy_blocks, pa_decode) validate their
+ *     host-side arguments synchronously, enqueue kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream) and return without synchronising.
+ *     Device pointers belong to the caller, who keeps them alive until the
+ *     stream has passed the call.  The library keeps no caller pointer after
+ *     a call returns (except a pool's caller-provided memory, see
+ *     pa_alloc_pool).
+ *   - Device-resident indices (block tables, context lengths, slot mappings,
+ *     copy pairs) are not read on the host unless the environment variable
+ *     PA_DEBUG_VALIDATE=1 is set; then each device call copies them to the
+ *     host, synchronises the stream and rejects out-of-range or aliasing
+ *     entries with PA_ERR_INVALID before launching anything.
+ *   - Kernel faults are asynchronous and surface as PA_ERR_HIP from a later
+ *     call that checks the stream.
+ *   - Sizes and indices are int32_t; byte counts int64_t.
+ *
+ * Pool layout (device memory, one array each for K and V):
+ *     [num_blocks][kv_heads][block_size][head_dim] elements of the pool dtype,
+ *   so the tile of one (block, kv-head) is block_size*head_dim contiguous
+ *   elements (the pages ask only that each block be contiguous inside, [P2]
+ *   §4.2).  Slot s means (block s / block_size, offset s % block_size).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+#define PA_OK               0
+#define PA_ERR_INVALID     -1  /* bad size, pointer or index                   */
+#define PA_ERR_UNSUPPORTED -2  /* dtype / head_dim / block_size / group size   */
+#define PA_ERR_NO_BLOCKS   -3  /* free list cannot supply the blocks; no change */
+#define PA_ERR_READ_ONLY   -4  /* write into a shared (refcount > 1) block      */
+#define PA_ERR_NOT_FOUND   -5  /* unknown sequence id                           */
+#define PA_ERR_EXISTS      -6  /* sequence id already present                   */
+#define PA_ERR_HIP         -7  /* HIP runtime or kernel launch failure          */
+#define PA_ERR_NO_MEMORY   -8  /* device or host allocation failed              */
+
+typedef int32_t pa_dtype;
+#define PA_F32  0
+#define PA_F16  1
+#define PA_BF16 2
+
+typedef struct pa_pool pa_pool;
+typedef struct pa_bm pa_bm;
+
+/* Message for the calling thread's most recent error ("" if none). */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* KV block pool ([P1] "Paged Attention 的工作原理"; [P2] §2.1, §3.1, §4.2)   */
+/* ------------------------------------------------------------------------ */
+
+/* Describe (and optionally allocate) a pool of num_blocks blocks.
+ *   block_size ∈ {4, 8, 16, 32, 64}; head_dim ∈ {64, 128};
+ *   dtype ∈ {PA_F32, PA_F16, PA_BF16}; kv_heads ≥ 1;
+ *   num_blocks * block_size < 2^31 (slots are int32).
+ *   k_mem, v_mem: both NULL → the library allocates both arrays on the current
+ *   HIP device and frees them in pa_free_pool; both non-NULL → caller-owned
+ *   device memory of at least num_blocks * pa block bytes each, 256-byte
+ *   aligned, which must outlive the pool.  Contents start undefined.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_MEMORY. */
+pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t kv_heads,
+                        int32_t head_dim, pa_dtype dtype, void* k_mem, void* v_mem,
+                        pa_pool** out);
+
+/* Release the descriptor (and the arrays if the library allocated them).
+ * NULL is ignored.  Work already enqueued on the pool must have completed. */
+void pa_free_pool(pa_pool* pool);
+
+/* Device addresses of the K and V arrays and the bytes of one block of one of
+ * them (kv_heads * block_size * head_dim * element size).  Any out pointer may
+ * be NULL. */
+pa_status pa_pool_info(const pa_pool* pool, void** k, void** v, int64_t* block_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* Slot-mapped KV write — decode step 3 of [P2] §3.2.2, prefill of §3.2.1   */
+/* ------------------------------------------------------------------------ */
+
+/* For each row i < n with slot_mapping[i] ≥ 0, copy k_new[i] and v_new[i]
+ * (each kv_heads*head_dim elements of the pool dtype) into that slot of every
+ * kv-head's tile; rows with slot -1 are skipped.  Bit-exact byte copy.
+ *   k_new, v_new: device [n][kv_heads][head_dim], contiguous, 16-byte aligned.
+ *   slot_mapping: device int32[n]; live slots must be distinct and
+ *   < num_blocks*block_size (checked only under PA_DEBUG_VALIDATE).
+ * n = 0 is a no-op.  Errors: PA_ERR_INVALID, PA_ERR_HIP. */
+pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, int32_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Copy-on-write block copy ([P2] §3.4)                                     */
+/* ------------------------------------------------------------------------ */
+
+/* For each of the n (src, dst) pairs, copy block src to block dst (K and V,
+ * every kv-head, every slot).  Pairs act as if simultaneous.
+ *   pairs: device int32[n][2]; destinations must be distinct and disjoint
+ *   from sources, all in [0, num_blocks) (checked only under
+ *   PA_DEBUG_VALIDATE).  Enqueue before the pa_write_kv that writes into the
+ *   copies; stream order then makes the write land on the copied block.
+ * n = 0 is a no-op.  Errors: PA_ERR_INVALID, PA_ERR_HIP. */
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Paged decode attention ([P2] §1.1, §3.2.2 step 4, §4.1, §4.2)            */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace pa_decode needs for these sizes (0 when every
+ * sequence fits one partition).  partition_tokens as for pa_decode. */
+pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
+                                    int32_t max_context_len, int32_t partition_tokens,
+                                    int64_t* bytes);
+
+/* The partition length pa_decode will use for these sizes (resolves 0 =
+ * automatic). */
+pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
+                                     int32_t max_context_len, int32_t partition_tokens,
+                                     int32_t* resolved);
+
+/* out[s][h] = softmax(q[s][h] · K_sᵀ · scale) · V_s over the context_lens[s]
+ * tokens of sequence s, whose token t lives at slot
+ * block_tables[s*block_table_stride + t/block_size]*block_size + t%block_size.
+ *   q: device [num_seqs][q_heads][head_dim] in the pool dtype.
+ *   out: device [num_seqs][q_heads][head_dim] in out_dtype (the pool dtype or
+ *     PA_F32); rounding to fp16/bf16 is round-to-nearest-even.
+ *   q_heads must be a multiple of kv_heads with group q_heads/kv_heads ∈
+ *     {1, 2, 4, 8}; query head h reads kv-head h / group.
+ *   block_tables: device int32; row s holds ≥ ceil(context_lens[s]/block_size)
+ *     valid block ids; block_table_stride ≥ ceil(max_context_len/block_size).
+ *   context_lens: device int32[num_seqs], each in [0, max_context_len];
+ *     a length of 0 gives a zero row.  Slots past the length are never used.
+ *   max_context_len: host-known bound that sizes the launch grid.
+ *   scale: the logit scale; ≤ 0 selects 1/sqrt(head_dim).
+ *   partition_tokens: tokens per work partition (split-K over the context);
+ *     0 = automatic, else a positive multiple of block_size.  Sequences
+ *     longer than one partition are combined by a second reduce kernel.
+ *   workspace: device memory of ≥ pa_decode_workspace_bytes(...) bytes
+ *     (fp32 partial max/sum/output per partition); may be NULL when that is 0.
+ * A length above max_context_len, or a block id outside the pool, yields NaN
+ * in that sequence's output rows instead of a memory access out of bounds.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
+pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q,
+                    int32_t num_seqs, int32_t q_heads, const int32_t* block_tables,
+                    int32_t block_table_stride, const int32_t* context_lens,
+                    int32_t max_context_len, float scale, int32_t partition_tokens,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block manager ([P2] §3.2, §3.3, §3.4; [P1] "跨请求的内存共享")        */
+/* Pure host code: needs no GPU.  Not thread-safe per instance.              */
+/* ------------------------------------------------------------------------ */
+/* Policy (fixed so results are reproducible):
+ *   - FIFO free list, initially initial_free_order (NULL = 0..num_blocks-1);
+ *     allocation takes the head, release appends to the tail in table order.
+ *   - Prefill of n tokens takes ceil(n/block_size) blocks ([P2] §3.2.1).
+ *   - Append: if the length is a multiple of block_size a new block is
+ *     appended; otherwise, if the last block's refcount is > 1, it is copied
+ *     to a new block (a copy-on-write pair), the table entry is repointed and
+ *     the old count drops by one.  Sequences in a batch are visited in order,
+ *     so the last of k sharers writes in place ([P2] §3.2.2, §3.4).
+ *   - A block is read-only while its refcount is > 1.
+ *   - Calls that fail leave the manager unchanged. */
+
+typedef struct pa_bm_stats_t {
+  int32_t num_blocks, block_size;
+  int32_t free_blocks;     /* blocks on the free list                        */
+  int32_t used_blocks;     /* blocks with refcount > 0                       */
+  int32_t shared_blocks;   /* blocks with refcount > 1                       */
+  int32_t num_seqs;
+  int64_t logical_tokens;  /* sum of sequence lengths                        */
+  int64_t logical_blocks;  /* sum of block-table lengths                     */
+  int64_t filled_slots;    /* slots of used blocks holding a token (unique)  */
+  int64_t cow_copies;      /* copy-on-write pairs emitted so far             */
+} pa_bm_stats_t;
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size,
+                       const int32_t* initial_free_order, pa_bm** out);
+void pa_bm_destroy(pa_bm* bm);
+
+/* Prefill allocation of num_tokens ≥ 0 tokens for a new sequence.
+ * Errors: PA_ERR_EXISTS, PA_ERR_INVALID, PA_ERR_NO_BLOCKS. */
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t num_tokens);
+
+/* child shares every block of parent (each refcount +1) and its length
+ * ([P1] "跨请求的内存共享": parallel samples, beam branches).
+ * Errors: PA_ERR_NOT_FOUND, PA_ERR_EXISTS. */
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
+
+/* Append one token to one sequence.  *slot receives its slot; *cow_src and
+ * *cow_dst receive the copy pair or -1.  Errors: PA_ERR_NOT_FOUND,
+ * PA_ERR_NO_BLOCKS. */
+pa_status pa_bm_append_slot(pa_bm* bm, int64_t seq_id, int32_t* slot, int32_t* cow_src,
+                            int32_t* cow_dst);
+
+/* Batched decode-step append for n distinct sequences, all or nothing.
+ * Outputs (host memory, caller-owned, any may be NULL):
+ *   slot_mapping int32[n]; cow_pairs int32[n][2] with *n_cow pairs filled in
+ *   decision order; block_tables int32[n][stride] (rows padded with -1;
+ *   PA_ERR_INVALID if a table is longer than stride); context_lens int32[n]
+ *   (lengths after the append).
+ * Errors: PA_ERR_INVALID (duplicate ids, bad stride), PA_ERR_NOT_FOUND,
+ * PA_ERR_NO_BLOCKS. */
+pa_status pa_bm_step(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* slot_mapping,
+                     int32_t* cow_pairs, int32_t* n_cow, int32_t* block_tables, int32_t stride,
+                     int32_t* context_lens);
+
+/* Release a sequence: refcounts drop; blocks reaching 0 rejoin the free list.
+ * Errors: PA_ERR_NOT_FOUND. */
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
+
+/* Copy a sequence's block table (up to cap entries) into out; *n_blocks and
+ * *n_tokens receive its table length and token count.  PA_ERR_INVALID if
+ * cap is too small (n_blocks is still set).  Errors: PA_ERR_NOT_FOUND. */
+pa_status pa_bm_block_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t cap,
+                            int32_t* n_blocks, int32_t* n_tokens);
+
+/* Slots of tokens [first, first+count) of a sequence (for a prefill
+ * pa_write_kv).  Errors: PA_ERR_NOT_FOUND, PA_ERR_INVALID (range). */
+pa_status pa_bm_token_slots(const pa_bm* bm, int64_t seq_id, int32_t first, int32_t count,
+                            int32_t* out);
+
+/* Rows of block tables and lengths for n sequences, as pa_bm_step writes
+ * them, without appending. */
+pa_status pa_bm_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* block_tables,
+                       int32_t stride, int32_t* context_lens);
+
+pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc);
+
+/* Free-list contents from head to tail (up to cap entries); *n receives the
+ * number of free blocks. */
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
+
+pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,484 @@
+// C ABI of libpa.so (declared in include/pa.h): argument validation, pool
+// ownership, decode planning and kernel launches, and the block-manager
+// wrappers.  Host code only; the kernels live in the .hip files.
+#include "pa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "block_manager.h"
+#include "launch.h"
+
+struct pa_pool {
+  pa::PoolDesc d;
+  bool owns;
+};
+
+struct pa_bm {
+  explicit pa_bm(int32_t nb, int32_t bs, const std::vector<int32_t>& order) : impl(nb, bs, order) {}
+  pa::BlockManager impl;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Read on every device call so a process can switch it per call.
+bool debug_validate() {
+  const char* v = std::getenv("PA_DEBUG_VALIDATE");
+  return v && *v && std::strcmp(v, "0") != 0;
+}
+
+int32_t env_int(const char* name, int32_t dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return static_cast<int32_t>(std::strtol(v, nullptr, 10));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool supported_block_size(int32_t bs) { return bs == 4 || bs == 8 || bs == 16 || bs == 32 || bs == 64; }
+
+pa_status map_bm(pa::BmResult r, const std::string& why) {
+  switch (r) {
+    case pa::BmResult::ok: return PA_OK;
+    case pa::BmResult::invalid: return fail(PA_ERR_INVALID, why);
+    case pa::BmResult::no_blocks: return fail(PA_ERR_NO_BLOCKS, why);
+    case pa::BmResult::not_found: return fail(PA_ERR_NOT_FOUND, why);
+    case pa::BmResult::exists: return fail(PA_ERR_EXISTS, why);
+  }
+  return fail(PA_ERR_INVALID, why);
+}
+
+// Copy n int32 from device to host on `stream` and wait (debug validation only).
+pa_status fetch_ints(const int32_t* dev, int64_t n, std::vector<int32_t>* host, hipStream_t stream) {
+  host->resize(static_cast<size_t>(n));
+  if (n == 0) return PA_OK;
+  hipError_t e = hipMemcpyAsync(host->data(), dev, static_cast<size_t>(n) * sizeof(int32_t), hipMemcpyDeviceToHost,
+                                stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "PA_DEBUG_VALIDATE copy");
+  return PA_OK;
+}
+
+// Partition length for a decode of these sizes: an explicit multiple of the
+// block size, the PA_PARTITION_TOKENS override, or 512 tokens.
+pa_status resolve_partition(const pa_pool* pool, int32_t requested, int32_t* out) {
+  int32_t p = requested > 0 ? requested : env_int("PA_PARTITION_TOKENS", 512);
+  if (p <= 0 || p % pool->d.block_size != 0) {
+    return fail(PA_ERR_INVALID, "partition_tokens must be a positive multiple of block_size (" +
+                                    std::to_string(pool->d.block_size) + ")");
+  }
+  *out = p;
+  return PA_OK;
+}
+
+int64_t workspace_for(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_parts) {
+  if (max_parts <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * max_parts;
+  const int64_t ml = ((rows * 2 * 4) + 255) / 256 * 256;
+  return ml + rows * pool->d.head_dim * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+// pool
+// ---------------------------------------------------------------------------
+pa_status pa_alloc_pool(int32_t num_blocks, int32_t block_size, int32_t kv_heads, int32_t head_dim,
+                        pa_dtype dtype, void* k_mem, void* v_mem, pa_pool** out) {
+  if (!out) return fail(PA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || kv_heads <= 0) return fail(PA_ERR_INVALID, "num_blocks and kv_heads must be positive");
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype");
+  if (!supported_block_size(block_size)) return fail(PA_ERR_UNSUPPORTED, "block_size must be 4, 8, 16, 32 or 64");
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31))
+    return fail(PA_ERR_INVALID, "num_blocks * block_size must be < 2^31");
+  if ((k_mem == nullptr) != (v_mem == nullptr)) return fail(PA_ERR_INVALID, "pass both k_mem and v_mem or neither");
+  if (k_mem && (!aligned(k_mem, 256) || !aligned(v_mem, 256)))
+    return fail(PA_ERR_INVALID, "pool memory must be 256-byte aligned");
+  pa::PoolDesc d{};
+  d.num_blocks = num_blocks;
+  d.block_size = block_size;
+  d.kv_heads = kv_heads;
+  d.head_dim = head_dim;
+  d.dtype = dtype;
+  d.block_bytes = static_cast<int64_t>(kv_heads) * block_size * head_dim * pa::elem_bytes(dtype);
+  bool owns = false;
+  if (!k_mem) {
+    const size_t bytes = static_cast<size_t>(d.block_bytes) * num_blocks;
+    hipError_t e = hipMalloc(&d.k, bytes);
+    if (e != hipSuccess) return fail(PA_ERR_NO_MEMORY, std::string("hipMalloc K: ") + hipGetErrorString(e));
+    e = hipMalloc(&d.v, bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(d.k);
+      return fail(PA_ERR_NO_MEMORY, std::string("hipMalloc V: ") + hipGetErrorString(e));
+    }
+    owns = true;
+  } else {
+    d.k = k_mem;
+    d.v = v_mem;
+  }
+  *out = new pa_pool{d, owns};
+  return PA_OK;
+}
+
+void pa_free_pool(pa_pool* pool) {
+  if (!pool) return;
+  if (pool->owns) {
+    (void)hipFree(pool->d.k);
+    (void)hipFree(pool->d.v);
+  }
+  delete pool;
+}
+
+pa_status pa_pool_info(const pa_pool* pool, void** k, void** v, int64_t* block_bytes) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (k) *k = pool->d.k;
+  if (v) *v = pool->d.v;
+  if (block_bytes) *block_bytes = pool->d.block_bytes;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// KV write / block copy
+// ---------------------------------------------------------------------------
+pa_status pa_write_kv(pa_pool* pool, const void* k_new, const void* v_new, const int32_t* slot_mapping, int32_t n,
+                      void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID, "n must be >= 0");
+  if (n == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID, "k_new/v_new must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_validate()) {
+    std::vector<int32_t> slots;
+    if (pa_status s = fetch_ints(slot_mapping, n, &slots, st)) return s;
+    const int64_t total = static_cast<int64_t>(pool->d.num_blocks) * pool->d.block_size;
+    std::vector<char> seen(static_cast<size_t>(total), 0);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t sl = slots[i];
+      if (sl < -1 || sl >= total) return fail(PA_ERR_INVALID, "slot " + std::to_string(sl) + " outside the pool");
+      if (sl >= 0 && seen[sl]++) return fail(PA_ERR_INVALID, "slot " + std::to_string(sl) + " written twice");
+    }
+  }
+  hipError_t e = pa::launch_write_kv(pool->d, k_new, v_new, slot_mapping, n, st);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
+}
+
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID, "n must be >= 0");
+  if (n == 0) return PA_OK;
+  if (!pairs) return fail(PA_ERR_INVALID, "pairs is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_validate()) {
+    std::vector<int32_t> h;
+    if (pa_status s = fetch_ints(pairs, 2 * static_cast<int64_t>(n), &h, st)) return s;
+    std::vector<char> role(static_cast<size_t>(pool->d.num_blocks), 0);  // 1 = src, 2 = dst
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t a = h[2 * i], b = h[2 * i + 1];
+      if (a < 0 || a >= pool->d.num_blocks || b < 0 || b >= pool->d.num_blocks)
+        return fail(PA_ERR_INVALID, "copy pair outside the pool");
+      if (role[a] == 2) return fail(PA_ERR_INVALID, "a source block is also a destination");
+      role[a] = 1;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t b = h[2 * i + 1];
+      if (role[b] != 0) return fail(PA_ERR_INVALID, "destination block repeats or is a source");
+      role[b] = 2;
+    }
+  }
+  hipError_t e = pa::launch_copy_blocks(pool->d, pairs, n, st);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks launch");
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
+                                     int32_t partition_tokens, int32_t* resolved) {
+  (void)num_seqs;
+  (void)q_heads;
+  (void)max_context_len;
+  if (!pool || !resolved) return fail(PA_ERR_INVALID, "NULL pointer");
+  return resolve_partition(pool, partition_tokens, resolved);
+}
+
+pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
+                                    int32_t partition_tokens, int64_t* bytes) {
+  if (!pool || !bytes) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (num_seqs < 0 || q_heads <= 0 || max_context_len < 0) return fail(PA_ERR_INVALID, "negative size");
+  int32_t P;
+  if (pa_status s = resolve_partition(pool, partition_tokens, &P)) return s;
+  const int32_t max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, P)));
+  *bytes = workspace_for(pool, num_seqs, q_heads, max_parts);
+  return PA_OK;
+}
+
+pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs,
+                    int32_t q_heads, const int32_t* block_tables, int32_t block_table_stride,
+                    const int32_t* context_lens, int32_t max_context_len, float scale, int32_t partition_tokens,
+                    void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "num_seqs must be in [0, 65535]");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !context_lens) return fail(PA_ERR_INVALID, "NULL pointer");
+  const pa::PoolDesc& d = pool->d;
+  if (q_heads <= 0 || q_heads % d.kv_heads != 0)
+    return fail(PA_ERR_INVALID, "q_heads must be a positive multiple of kv_heads");
+  const int32_t group = q_heads / d.kv_heads;
+  if (!pa::decode_supported(d.dtype, d.head_dim, d.block_size, group))
+    return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(group) + " (supported: 1, 2, 4, 8)");
+  if (out_dtype != d.dtype && out_dtype != PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "out_dtype must be the pool dtype or PA_F32");
+  if (d.kv_heads > 65535 || q_heads > 65535) return fail(PA_ERR_INVALID, "kv_heads and q_heads must be <= 65535");
+  if (max_context_len < 0) return fail(PA_ERR_INVALID, "max_context_len must be >= 0");
+  if (block_table_stride < ceil_div(max_context_len, d.block_size))
+    return fail(PA_ERR_INVALID, "block_table_stride shorter than ceil(max_context_len / block_size)");
+  if (!aligned(q, 16)) return fail(PA_ERR_INVALID, "q must be 16-byte aligned");
+  int32_t P;
+  if (pa_status s = resolve_partition(pool, partition_tokens, &P)) return s;
+  const int32_t max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, P)));
+  const int64_t need = workspace_for(pool, num_seqs, q_heads, max_parts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return fail(PA_ERR_INVALID, "workspace must be 256-byte aligned and hold " + std::to_string(need) + " bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_validate()) {
+    std::vector<int32_t> lens, tables;
+    if (pa_status s = fetch_ints(context_lens, num_seqs, &lens, st)) return s;
+    if (pa_status s = fetch_ints(block_tables, static_cast<int64_t>(num_seqs) * block_table_stride, &tables, st))
+      return s;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      if (lens[i] < 0 || lens[i] > max_context_len)
+        return fail(PA_ERR_INVALID, "context_lens[" + std::to_string(i) + "] outside [0, max_context_len]");
+      const int64_t nblk = ceil_div(lens[i], d.block_size);
+      for (int64_t j = 0; j < nblk; ++j) {
+        const int32_t b = tables[static_cast<size_t>(i) * block_table_stride + j];
+        if (b < 0 || b >= d.num_blocks)
+          return fail(PA_ERR_INVALID, "block_tables[" + std::to_string(i) + "][" + std::to_string(j) + "] = " +
+                                          std::to_string(b) + " outside the pool");
+      }
+    }
+  }
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.block_tables = block_tables;
+  a.table_stride = block_table_stride;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d.head_dim));
+  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);  // log2(e)
+  a.partition_tokens = P;
+  a.max_parts = max_parts;
+  if (need > 0) {
+    const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * max_parts;
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((rows * 2 * 4) + 255) / 256 * 256);
+  }
+  hipError_t e = pa::launch_decode(d, a, st);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
+}
+
+// ---------------------------------------------------------------------------
+// block manager
+// ---------------------------------------------------------------------------
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order, pa_bm** out) {
+  if (!out) return fail(PA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0) return fail(PA_ERR_INVALID, "num_blocks and block_size must be positive");
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t{1} << 31))
+    return fail(PA_ERR_INVALID, "num_blocks * block_size must be < 2^31");
+  std::vector<int32_t> order;
+  if (initial_free_order) {
+    if (!pa::BlockManager::is_permutation(initial_free_order, num_blocks))
+      return fail(PA_ERR_INVALID, "initial_free_order is not a permutation of 0..num_blocks-1");
+    order.assign(initial_free_order, initial_free_order + num_blocks);
+  }
+  try {
+    *out = new pa_bm(num_blocks, block_size, order);
+  } catch (...) {
+    return fail(PA_ERR_NO_MEMORY, "block manager allocation");
+  }
+  return PA_OK;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id, int32_t num_tokens) {
+  if (!bm) return fail(PA_ERR_INVALID, "bm is NULL");
+  std::string why;
+  return map_bm(bm->impl.add_seq(seq_id, num_tokens, &why), why);
+}
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
+  if (!bm) return fail(PA_ERR_INVALID, "bm is NULL");
+  std::string why;
+  return map_bm(bm->impl.fork(parent_id, child_id, &why), why);
+}
+
+pa_status pa_bm_append_slot(pa_bm* bm, int64_t seq_id, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+  if (!bm || !slot || !cow_src || !cow_dst) return fail(PA_ERR_INVALID, "NULL pointer");
+  std::string why;
+  return map_bm(bm->impl.append_slot(seq_id, slot, cow_src, cow_dst, &why), why);
+}
+
+static void write_rows(const pa::BlockManager& m, const int64_t* ids, int32_t n, int32_t* tables, int32_t stride,
+                       int32_t* lens) {
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t len = 0;
+    const std::vector<int32_t>* t = m.table(ids[i], &len);
+    if (tables) {
+      int32_t* row = tables + static_cast<int64_t>(i) * stride;
+      const int32_t nb = static_cast<int32_t>(t->size());
+      std::memcpy(row, t->data(), sizeof(int32_t) * nb);
+      for (int32_t j = nb; j < stride; ++j) row[j] = -1;
+    }
+    if (lens) lens[i] = len;
+  }
+}
+
+pa_status pa_bm_step(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* slot_mapping, int32_t* cow_pairs,
+                     int32_t* n_cow, int32_t* block_tables, int32_t stride, int32_t* context_lens) {
+  if (!bm) return fail(PA_ERR_INVALID, "bm is NULL");
+  if (n < 0 || (n > 0 && !seq_ids)) return fail(PA_ERR_INVALID, "bad batch");
+  if (n_cow) *n_cow = 0;
+  const int32_t bs = bm->impl.block_size();
+  if (block_tables) {
+    if (stride <= 0) return fail(PA_ERR_INVALID, "stride must be positive");
+    for (int32_t i = 0; i < n; ++i) {
+      int32_t len = 0;
+      if (bm->impl.table(seq_ids[i], &len) && ceil_div(static_cast<int64_t>(len) + 1, bs) > stride)
+        return fail(PA_ERR_INVALID, "stride shorter than sequence " + std::to_string(seq_ids[i]) + "'s table");
+    }
+  }
+  std::vector<int32_t> pairs;
+  std::string why;
+  pa::BmResult r = bm->impl.step(seq_ids, n, slot_mapping, &pairs, &why);
+  if (r != pa::BmResult::ok) return map_bm(r, why);
+  if (cow_pairs && !pairs.empty()) std::memcpy(cow_pairs, pairs.data(), sizeof(int32_t) * pairs.size());
+  if (n_cow) *n_cow = static_cast<int32_t>(pairs.size() / 2);
+  write_rows(bm->impl, seq_ids, n, block_tables, stride, context_lens);
+  return PA_OK;
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
+  if (!bm) return fail(PA_ERR_INVALID, "bm is NULL");
+  std::string why;
+  return map_bm(bm->impl.free_seq(seq_id, &why), why);
+}
+
+pa_status pa_bm_block_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t cap, int32_t* n_blocks,
+                            int32_t* n_tokens) {
+  if (!bm) return fail(PA_ERR_INVALID, "bm is NULL");
+  int32_t len = 0;
+  const std::vector<int32_t>* t = bm->impl.table(seq_id, &len);
+  if (!t) return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seq_id));
+  const int32_t nb = static_cast<int32_t>(t->size());
+  if (n_blocks) *n_blocks = nb;
+  if (n_tokens) *n_tokens = len;
+  if (out) {
+    if (cap < nb) return fail(PA_ERR_INVALID, "cap smaller than the table");
+    std::memcpy(out, t->data(), sizeof(int32_t) * nb);
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_token_slots(const pa_bm* bm, int64_t seq_id, int32_t first, int32_t count, int32_t* out) {
+  if (!bm || (count > 0 && !out)) return fail(PA_ERR_INVALID, "NULL pointer");
+  int32_t len = 0;
+  const std::vector<int32_t>* t = bm->impl.table(seq_id, &len);
+  if (!t) return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seq_id));
+  if (first < 0 || count < 0 || static_cast<int64_t>(first) + count > len)
+    return fail(PA_ERR_INVALID, "token range outside the sequence");
+  const int32_t bs = bm->impl.block_size();
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t tok = first + i;
+    out[i] = (*t)[tok / bs] * bs + tok % bs;
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* block_tables, int32_t stride,
+                       int32_t* context_lens) {
+  if (!bm || n < 0 || (n > 0 && !seq_ids)) return fail(PA_ERR_INVALID, "bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    const std::vector<int32_t>* t = bm->impl.table(seq_ids[i], nullptr);
+    if (!t) return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seq_ids[i]));
+    if (block_tables && static_cast<int32_t>(t->size()) > stride)
+      return fail(PA_ERR_INVALID, "stride shorter than sequence " + std::to_string(seq_ids[i]) + "'s table");
+  }
+  write_rows(bm->impl, seq_ids, n, block_tables, stride, context_lens);
+  return PA_OK;
+}
+
+pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc) {
+  if (!bm || !rc) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (block < 0 || block >= bm->impl.num_blocks()) return fail(PA_ERR_INVALID, "block outside the pool");
+  *rc = bm->impl.refcount(block);
+  return PA_OK;
+}
+
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm) return fail(PA_ERR_INVALID, "bm is NULL");
+  const auto& fl = bm->impl.free_list();
+  const int32_t cnt = static_cast<int32_t>(fl.size());
+  if (n) *n = cnt;
+  if (out) {
+    if (cap < cnt) return fail(PA_ERR_INVALID, "cap smaller than the free list");
+    int32_t i = 0;
+    for (int32_t b : fl) out[i++] = b;
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
+  if (!bm || !out) return fail(PA_ERR_INVALID, "NULL pointer");
+  const pa::BmStats s = bm->impl.stats();
+  out->num_blocks = s.num_blocks;
+  out->block_size = s.block_size;
+  out->free_blocks = s.free_blocks;
+  out->used_blocks = s.used_blocks;
+  out->shared_blocks = s.shared_blocks;
+  out->num_seqs = s.num_seqs;
+  out->logical_tokens = s.logical_tokens;
+  out->logical_blocks = s.logical_blocks;
+  out->filled_slots = s.filled_slots;
+  out->cow_copies = s.cow_copies;
+  return PA_OK;
+}
+
+}  // extern "C"
+
+namespace pa {
+bool decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
+  return (dtype == kF32 || dtype == kF16 || dtype == kBF16) && (head_dim == 64 || head_dim == 128) &&
+         supported_block_size(block_size) && (group == 1 || group == 2 || group == 4 || group == 8);
+}
+}  // namespace pa

@@ -1,0 +1,68 @@
+// Host block manager: free list, refcounts, fork, copy-on-write and slot
+// assignment for the paged KV cache.  Pure C++ (no HIP), so it runs and is
+// tested without a GPU.
+//
+// Pages: [P2] "PagedAttention：操作系统级 KV 缓存虚拟内存管理" §3.2.1 (prefill
+// takes ⌈n/bs⌉ blocks, last part-filled), §3.2.2 (decode append: a full last
+// block means a new block), §3.3 (one free pool, blocks recycled on release),
+// §3.4 (refcounted sharing, read-only shared blocks, copy before write);
+// [P1] "Paged Attention：大模型推理显存优化的核心方案", "跨请求的内存共享"
+// (forked samples / beams share blocks).
+#pragma once
+
+#include <cstdint>
+#include <deque>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+namespace pa {
+
+enum class BmResult { ok, invalid, no_blocks, not_found, exists };
+
+struct BmStats {
+  int32_t num_blocks, block_size, free_blocks, used_blocks, shared_blocks, num_seqs;
+  int64_t logical_tokens, logical_blocks, filled_slots, cow_copies;
+};
+
+class BlockManager {
+ public:
+  // initial_free_order: permutation of 0..num_blocks-1 (validated by caller
+  // via is_permutation) or empty for the identity order.
+  BlockManager(int32_t num_blocks, int32_t block_size, const std::vector<int32_t>& initial_free_order);
+
+  static bool is_permutation(const int32_t* order, int32_t n);
+
+  BmResult add_seq(int64_t id, int32_t num_tokens, std::string* why);
+  BmResult fork(int64_t parent, int64_t child, std::string* why);
+  BmResult append_slot(int64_t id, int32_t* slot, int32_t* cow_src, int32_t* cow_dst, std::string* why);
+  // Batched append in batch order, all or nothing.  slots[n]; cow pairs are
+  // appended to `pairs` as src, dst.
+  BmResult step(const int64_t* ids, int32_t n, int32_t* slots, std::vector<int32_t>* pairs, std::string* why);
+  BmResult free_seq(int64_t id, std::string* why);
+
+  const std::vector<int32_t>* table(int64_t id, int32_t* length) const;
+  int32_t refcount(int32_t block) const { return rc_[block]; }
+  const std::deque<int32_t>& free_list() const { return free_; }
+  BmStats stats() const;
+
+  int32_t num_blocks() const { return num_blocks_; }
+  int32_t block_size() const { return block_size_; }
+
+ private:
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t length = 0;
+  };
+  int32_t pop_free();
+  void append_unchecked(Seq& s, int32_t* slot, int32_t* cow_src, int32_t* cow_dst);
+
+  int32_t num_blocks_, block_size_;
+  std::deque<int32_t> free_;
+  std::vector<int32_t> rc_;
+  std::unordered_map<int64_t, Seq> seqs_;
+  int64_t cow_copies_ = 0;
+  std::vector<int32_t> drop_scratch_;  // per-block refcount drops during a step's dry run
+};
+
+}  // namespace pa

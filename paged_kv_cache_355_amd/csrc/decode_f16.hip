@@ -1,0 +1,10 @@
+// Decode kernels instantiated for f16 pools (see decode_impl.h).
+#include "decode_impl.h"
+
+namespace pa {
+
+hipError_t launch_decode_f16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
+  return dec::launch_dtype<kF16>(p, a, stream);
+}
+
+}  // namespace pa

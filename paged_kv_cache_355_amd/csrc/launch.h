@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace pa {
+
+enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+inline int32_t elem_bytes(int32_t dt) { return dt == kF32 ? 4 : 2; }
+
+struct PoolDesc {
+  int32_t num_blocks, block_size, kv_heads, head_dim, dtype;
+  void* k;
+  void* v;
+  int64_t block_bytes;  // kv_heads * block_size * head_dim * elem (one tensor)
+};
+
+struct DecodeArgs {
+  void* out;
+  int32_t out_dtype;
+  const void* q;
+  int32_t num_seqs, q_heads;
+  const int32_t* block_tables;
+  int32_t table_stride;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  float scale_log2;        // logit scale × log2(e)
+  int32_t partition_tokens;
+  int32_t max_parts;       // partitions covering max_context_len
+  float* part_ml;          // [num_seqs][q_heads][max_parts][2]   (max, sum)
+  float* part_o;           // [num_seqs][q_heads][max_parts][head_dim]
+};
+
+// True when the decode kernels are instantiated for these sizes.
+bool decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
+
+hipError_t launch_write_kv(const PoolDesc& p, const void* k_new, const void* v_new, const int32_t* slots,
+                           int32_t n, hipStream_t stream);
+hipError_t launch_copy_blocks(const PoolDesc& p, const int32_t* pairs, int32_t n, hipStream_t stream);
+hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
+
+// Per-dtype decode launchers (decode_<dtype>.hip).
+hipError_t launch_decode_f32(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,173 @@
+"""The library's C++ block manager against the oracle's, bit for bit.
+
+Both run the same call scripts; every block table, length, slot, copy pair,
+refcount and the free list must agree exactly.  Needs the built libpa.so but
+no GPU.
+"""
+import numpy as np
+import pytest
+from hypothesis import settings, strategies as st
+from hypothesis.stateful import RuleBasedStateMachine, rule, invariant, precondition
+
+import paged_kv_cache_355_amd as pk
+from oracle.block_manager import OracleBlockManager, NoBlocksError
+from workloads import WORKLOADS, make_scenario
+
+
+def assert_same_state(lib_bm, ora):
+    assert lib_bm.free_list() == list(ora.free)
+    assert [lib_bm.refcount(b) for b in range(ora.num_blocks)] == ora.rc
+    for sid in ora.seqs:
+        assert lib_bm.block_table(sid) == ora.block_table(sid)
+    st_ = lib_bm.stats()
+    ost = ora.stats()
+    for k, v in ost.items():
+        assert st_[k] == v, k
+
+
+def run_ops(lib_bm, ora, ops):
+    for op in ops:
+        if op[0] == "add":
+            lib_bm.add_seq(op[1], op[2])
+            ora.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            lib_bm.fork(op[1], op[2])
+            ora.fork(op[1], op[2])
+        elif op[0] == "step":
+            s1, p1, _, _ = lib_bm.step(op[1])
+            s2, p2 = ora.step(op[1])
+            assert s1.tolist() == s2
+            assert [tuple(x) for x in p1.tolist()] == p2
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_scripts_agree(name):
+    w = WORKLOADS[name]
+    sc = make_scenario(w)
+    lib_bm = pk.BlockManager(sc.num_blocks, w.block_size, sc.free_order)
+    ora = OracleBlockManager(sc.num_blocks, w.block_size, sc.free_order)
+    run_ops(lib_bm, ora, sc.all_ops())
+    # the measured step, with padded tables as the device sees them
+    stride = max(-(-(n + 1) // w.block_size) for n in sc.lengths_before.values())
+    slots, pairs, tables, lens = lib_bm.step(sc.measured, stride=stride)
+    o_slots, o_pairs = ora.step(sc.measured)
+    assert slots.tolist() == o_slots and [tuple(p) for p in pairs.tolist()] == o_pairs
+    assert tables.tolist() == ora.padded_tables(sc.measured, stride)
+    assert lens.tolist() == [ora.length(s) for s in sc.measured]
+    assert lens.tolist() == [sc.lengths_before[s] + 1 for s in sc.measured]
+    assert_same_state(lib_bm, ora)
+
+
+def test_prefix_share_copy_step_emits_224_pairs():
+    w = WORKLOADS["prefix_share_fp16"]
+    sc = make_scenario(w)
+    lib_bm = pk.BlockManager(sc.num_blocks, w.block_size, sc.free_order)
+    run_ops(lib_bm, OracleBlockManager(sc.num_blocks, w.block_size, sc.free_order), sc.setup)
+    _, pairs, _, _ = lib_bm.step(sc.cow_step)
+    assert pairs.shape == (32 * 7, 2)
+
+
+def test_exhaustion_is_all_or_nothing():
+    lib_bm = pk.BlockManager(3, 4, [0, 1, 2])
+    ora = OracleBlockManager(3, 4, [0, 1, 2])
+    run_ops(lib_bm, ora, [("add", 0, 2), ("fork", 0, 1), ("add", 2, 4)])
+    with pytest.raises(pk.NoBlocksError):
+        lib_bm.step([0, 1, 2])
+    with pytest.raises(NoBlocksError):
+        ora.step([0, 1, 2])
+    assert_same_state(lib_bm, ora)
+    with pytest.raises(pk.NoBlocksError):
+        lib_bm.add_seq(5, 9)
+    assert_same_state(lib_bm, ora)
+
+
+def test_step_rejects_short_stride_without_change():
+    lib_bm = pk.BlockManager(8, 4)
+    lib_bm.add_seq(0, 8)
+    before = lib_bm.block_table(0)
+    with pytest.raises(pk.PaError):
+        lib_bm.step([0], stride=2)           # after the append the table needs 3 entries
+    assert lib_bm.block_table(0) == before
+
+
+def test_bad_calls():
+    bm = pk.BlockManager(8, 4)
+    bm.add_seq(1, 3)
+    for call, code in [(lambda: bm.add_seq(1, 3), -6), (lambda: bm.fork(9, 2), -5), (lambda: bm.fork(1, 1), -6),
+                       (lambda: bm.step([1, 1]), -1), (lambda: bm.step([4]), -5), (lambda: bm.add_seq(3, -1), -1),
+                       (lambda: bm.refcount(8), -1), (lambda: bm.token_slots(1, 2, 5), -1)]:
+        with pytest.raises(pk.PaError) as e:
+            call()
+        assert e.value.code == code
+
+
+class ParityMachine(RuleBasedStateMachine):
+    def __init__(self):
+        super().__init__()
+        order = list(np.random.default_rng(3).permutation(20))
+        self.lib = pk.BlockManager(20, 4, order)
+        self.ora = OracleBlockManager(20, 4, order)
+        self.next_id = 100
+
+    @rule(n=st.integers(0, 11))
+    def add(self, n):
+        sid = self.next_id
+        self.next_id += 1
+        try:
+            self.ora.add_seq(sid, n)
+        except NoBlocksError:
+            with pytest.raises(pk.NoBlocksError):
+                self.lib.add_seq(sid, n)
+            return
+        self.lib.add_seq(sid, n)
+        assert self.lib.token_slots(sid).tolist() == self.ora.token_slots(sid)
+
+    @precondition(lambda self: self.ora.seqs)
+    @rule(data=st.data())
+    def fork(self, data):
+        parent = data.draw(st.sampled_from(sorted(self.ora.seqs)))
+        self.ora.fork(parent, self.next_id)
+        self.lib.fork(parent, self.next_id)
+        self.next_id += 1
+
+    @precondition(lambda self: self.ora.seqs)
+    @rule(data=st.data())
+    def step(self, data):
+        ids = data.draw(st.lists(st.sampled_from(sorted(self.ora.seqs)), min_size=1, unique=True))
+        try:
+            o_slots, o_pairs = self.ora.step(ids)
+        except NoBlocksError:
+            with pytest.raises(pk.NoBlocksError):
+                self.lib.step(ids)
+            return
+        slots, pairs, _, lens = self.lib.step(ids)
+        assert slots.tolist() == o_slots
+        assert [tuple(p) for p in pairs.tolist()] == o_pairs
+        assert lens.tolist() == [self.ora.length(s) for s in ids]
+
+    @precondition(lambda self: self.ora.seqs)
+    @rule(data=st.data())
+    def append_one(self, data):
+        sid = data.draw(st.sampled_from(sorted(self.ora.seqs)))
+        try:
+            want = self.ora.append_slot(sid)
+        except NoBlocksError:
+            with pytest.raises(pk.NoBlocksError):
+                self.lib.append_slot(sid)
+            return
+        assert self.lib.append_slot(sid) == want
+
+    @precondition(lambda self: self.ora.seqs)
+    @rule(data=st.data())
+    def free(self, data):
+        sid = data.draw(st.sampled_from(sorted(self.ora.seqs)))
+        self.ora.free_seq(sid)
+        self.lib.free_seq(sid)
+
+    @invariant()
+    def same_state(self):
+        assert_same_state(self.lib, self.ora)
+
+
+TestParityMachine = ParityMachine.TestCase
+TestParityMachine.settings = settings(max_examples=120, stateful_step_count=40, deadline=None)

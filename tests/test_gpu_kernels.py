@@ -1,0 +1,257 @@
+"""GPU parity of the HIP kernels against the oracle, on small seeded cases.
+
+Every case goes through the C ABI (libpa.so via the ctypes binding).  KV
+write and block copy must be bit-exact over the whole pool; decode must be
+within 1e-5 (fp32) or 2e-3 (fp16/bf16) of the fp64 oracle, element by element.
+Pools are poisoned with NaN everywhere no live token sits, so any read of a
+padding slot, an unallocated block or a table entry past the context shows
+up as a NaN.
+"""
+import os
+import zlib
+
+import numpy as np
+import torch  # noqa: F401  (first import can be slow on a fresh box; keep it out of test timeouts)
+import pytest
+
+from oracle.attention import paged_decode
+from oracle.kv_ops import write_kv as oracle_write_kv, copy_blocks as oracle_copy_blocks
+from oracle.block_manager import OracleBlockManager
+from tests.gpu_util import (to_torch, to_bits, out_to_f64, draw, build_case, run_decode, peak_key, TOL, NAN_BITS)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    os.environ["PA_DEBUG_VALIDATE"] = "1"
+    import paged_kv_cache_355_amd as pk
+    pk.lib()
+    yield pk
+
+
+# ----------------------------------------------------------------------------
+# KV write and copy-on-write copy: bit-exact over the whole pool
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("head_dim,block_size,kv_heads", [(64, 4, 1), (128, 16, 4), (128, 32, 2), (64, 64, 3)])
+def test_write_kv_bit_exact(gpu, dtype, head_dim, block_size, kv_heads):
+    import torch
+    pk = gpu
+    rng = np.random.default_rng(head_dim + block_size + kv_heads)
+    nb = 12
+    bits_t = np.uint32 if dtype == "f32" else np.uint16
+    hi = 2 ** 32 if dtype == "f32" else 2 ** 16
+    k0 = rng.integers(0, hi, size=(nb, kv_heads, block_size, head_dim), dtype=np.uint64).astype(bits_t)
+    v0 = rng.integers(0, hi, size=k0.shape, dtype=np.uint64).astype(bits_t)
+    n = 9
+    slots = rng.choice(nb * block_size, size=n, replace=False).astype(np.int32)
+    slots[[2, 5]] = -1
+    kn = rng.integers(0, hi, size=(n, kv_heads, head_dim), dtype=np.uint64).astype(bits_t)
+    vn = rng.integers(0, hi, size=kn.shape, dtype=np.uint64).astype(bits_t)
+    pool = pk.Pool(nb, block_size, kv_heads, head_dim, dtype, k=to_torch(k0, dtype), v=to_torch(v0, dtype))
+    pk.write_kv(pool, to_torch(kn, dtype), to_torch(vn, dtype), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    k_want, v_want = k0.copy(), v0.copy()
+    oracle_write_kv(k_want, v_want, kn, vn, slots)
+    assert np.array_equal(to_bits(pool.k, dtype), k_want)
+    assert np.array_equal(to_bits(pool.v, dtype), v_want)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("head_dim,block_size,kv_heads", [(64, 4, 1), (128, 16, 32), (128, 32, 1)])
+def test_copy_blocks_bit_exact(gpu, dtype, head_dim, block_size, kv_heads):
+    import torch
+    pk = gpu
+    rng = np.random.default_rng(7 * head_dim + block_size)
+    nb = 24
+    bits_t = np.uint32 if dtype == "f32" else np.uint16
+    hi = 2 ** 32 if dtype == "f32" else 2 ** 16
+    k0 = rng.integers(0, hi, size=(nb, kv_heads, block_size, head_dim), dtype=np.uint64).astype(bits_t)
+    v0 = rng.integers(0, hi, size=k0.shape, dtype=np.uint64).astype(bits_t)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:5], perm[5:10]], axis=1).astype(np.int32)
+    pairs = np.concatenate([pairs, [[perm[0], perm[10]]]]).astype(np.int32)   # one source copied twice
+    pool = pk.Pool(nb, block_size, kv_heads, head_dim, dtype, k=to_torch(k0, dtype), v=to_torch(v0, dtype))
+    pk.copy_blocks(pool, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    k_want, v_want = k0.copy(), v0.copy()
+    oracle_copy_blocks(k_want, v_want, pairs)
+    assert np.array_equal(to_bits(pool.k, dtype), k_want)
+    assert np.array_equal(to_bits(pool.v, dtype), v_want)
+
+
+def test_copy_then_write_follows_stream_order(gpu):
+    """A copy-on-write step: copy the shared block, then write the new token into the copy."""
+    import torch
+    pk = gpu
+    bm = OracleBlockManager(8, 4, list(range(8)))
+    bm.add_seq(0, 6)
+    bm.fork(0, 1)
+    rng = np.random.default_rng(11)
+    k0 = draw(rng, (8, 2, 4, 64), "f16", 1.0)
+    v0 = draw(rng, (8, 2, 4, 64), "f16", 1.0)
+    slots, pairs = bm.step([0, 1])
+    kn, vn = draw(rng, (2, 2, 64), "f16", 1.0), draw(rng, (2, 2, 64), "f16", 1.0)
+    pool = pk.Pool(8, 4, 2, 64, "f16", k=to_torch(k0, "f16"), v=to_torch(v0, "f16"))
+    pk.copy_blocks(pool, torch.tensor(pairs, dtype=torch.int32).cuda())
+    pk.write_kv(pool, to_torch(kn, "f16"), to_torch(vn, "f16"), torch.tensor(slots, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    k_want, v_want = k0.copy(), v0.copy()
+    oracle_copy_blocks(k_want, v_want, pairs)
+    oracle_write_kv(k_want, v_want, kn, vn, slots)
+    assert pairs == [(1, 2)]
+    assert np.array_equal(to_bits(pool.k, "f16"), k_want) and np.array_equal(to_bits(pool.v, "f16"), v_want)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def lengths_for(bs):
+    return [0, 1, bs - 1, bs + 1, 37, 130, 301]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("block_size", [4, 8, 16, 32, 64])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_matches_oracle(gpu, dtype, head_dim, block_size, group):
+    pk = gpu
+    kv_heads = 2
+    lens = lengths_for(block_size)
+    seed = zlib.crc32(repr((dtype, head_dim, block_size, group)).encode())
+    case = build_case(lens, kv_heads, group, head_dim, block_size, dtype, seed, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], dtype)
+    for partition in (2 * block_size, 0):                 # many partitions + reduce; one partition
+        got = out_to_f64(run_decode(pk, case, kv_heads, head_dim, block_size, dtype, out_dtype="f32",
+                                    partition_tokens=partition))
+        assert np.all(np.isfinite(got))
+        err = np.max(np.abs(got - want))
+        assert err <= TOL[dtype], (partition, err)
+        assert np.all(got[0] == 0.0)                        # empty context → zero row
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_decode_scaled_values_output_in_pool_dtype(gpu, dtype):
+    """N(0,1)/sqrt(128) values as in the benchmark shapes, output rounded to the pool dtype."""
+    pk = gpu
+    lens = [5, 77, 512, 513, 1030]
+    case = build_case(lens, 4, 1, 128, 16, dtype, 5, scale=1 / np.sqrt(128))
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], dtype)
+    got = out_to_f64(run_decode(pk, case, 4, 128, 16, dtype))
+    assert np.max(np.abs(got - want)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("group", [1, 8])
+def test_decode_peaked_logit_needs_max_subtraction(gpu, dtype, group):
+    """One key's logit is 100 (exp overflows fp32 without the running max)."""
+    pk = gpu
+    lens = [40, 700]
+    case = build_case(lens, 1, group, 128, 16, dtype, 17, scale=1.0)
+    peak_key(case, 1, 613, 0, group, 100.0, 128, dtype, 16)
+    peak_key(case, 0, 3, 0, group, 100.0, 128, dtype, 16)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], dtype)
+    for partition in (64, 0):
+        got = out_to_f64(run_decode(pk, case, 1, 128, 16, dtype, out_dtype="f32", partition_tokens=partition))
+        assert np.max(np.abs(got - want)) <= TOL[dtype]
+
+
+def test_decode_placement_invariance_is_bit_identical(gpu):
+    """Same logical K/V under different physical placements → identical bits."""
+    import torch
+    pk = gpu
+    lens = [3, 50, 333]
+    outs = []
+    for seed in range(3):
+        rng = np.random.default_rng(1234)
+        nb = sum(-(-n // 16) for n in lens) + 5
+        bm = OracleBlockManager(nb, 16, np.random.default_rng(seed).permutation(nb))
+        k_pool = np.full((nb, 2, 16, 128), NAN_BITS["bf16"], dtype=np.uint16)
+        v_pool = k_pool.copy()
+        for s, n in enumerate(lens):
+            bm.add_seq(s, n)
+            oracle_write_kv(k_pool, v_pool, draw(rng, (n, 2, 128), "bf16", 1.0), draw(rng, (n, 2, 128), "bf16", 1.0),
+                            bm.token_slots(s))
+        case = dict(k_pool=k_pool, v_pool=v_pool, q=draw(rng, (3, 8, 128), "bf16", 1.0), num_blocks=nb,
+                    tables=np.array(bm.padded_tables(range(3), 21, pad=-1), dtype=np.int32),
+                    lens=np.array(lens, dtype=np.int32))
+        outs.append(run_decode(pk, case, 2, 128, 16, "bf16", out_dtype="f32", partition_tokens=64).cpu())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_decode_shared_prefix_matches_private_copy(gpu):
+    pk = gpu
+    rng = np.random.default_rng(21)
+    bs, d, hkv = 16, 128, 2
+    bm = OracleBlockManager(64, bs, rng.permutation(64))
+    k_pool = np.full((64, hkv, bs, d), NAN_BITS["f16"], dtype=np.uint16)
+    v_pool = k_pool.copy()
+    bm.add_seq(0, 100)
+    k, v = draw(rng, (100, hkv, d), "f16", 1.0), draw(rng, (100, hkv, d), "f16", 1.0)
+    oracle_write_kv(k_pool, v_pool, k, v, bm.token_slots(0))
+    bm.fork(0, 1)
+    bm.add_seq(2, 100)
+    oracle_write_kv(k_pool, v_pool, k, v, bm.token_slots(2))
+    q1 = draw(rng, (1, hkv, d), "f16", 1.0)
+    case = dict(k_pool=k_pool, v_pool=v_pool, q=np.repeat(q1, 3, axis=0), num_blocks=64,
+                tables=np.array(bm.padded_tables([0, 1, 2], 7, pad=-1), dtype=np.int32),
+                lens=np.array([100, 100, 100], dtype=np.int32))
+    got = run_decode(pk, case, hkv, d, bs, "f16", out_dtype="f32").cpu()
+    assert (got[0] == got[1]).all() and (got[0] == got[2]).all()
+
+
+def test_decode_rejects_bad_metadata_under_validation(gpu):
+    import torch
+    pk = gpu
+    case = build_case([20, 9], 1, 1, 64, 4, "f32", 3)
+    case["tables"][1, 1] = case["num_blocks"] + 5
+    with pytest.raises(pk.PaError) as e:
+        run_decode(pk, case, 1, 64, 4, "f32")
+    assert "outside the pool" in str(e.value)
+    case = build_case([20, 9], 1, 1, 64, 4, "f32", 3)
+    pool = pk.Pool(case["num_blocks"], 4, 1, 64, "f32", k=to_torch(case["k_pool"], "f32"),
+                   v=to_torch(case["v_pool"], "f32"))
+    with pytest.raises(pk.PaError):
+        pk.decode(pool, to_torch(case["q"], "f32"), torch.from_numpy(case["tables"]).cuda(),
+                  torch.from_numpy(case["lens"]).cuda(), 10)         # a length above max_context_len
+
+
+def test_decode_bad_table_entry_gives_nan_not_a_fault(gpu):
+    """With host validation off, the kernel's own bounds check turns a block id
+    outside the pool into NaN output for that sequence only."""
+    pk = gpu
+    case = build_case([20, 9, 30], 1, 1, 64, 4, "f16", 4)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
+    case["tables"][1, 1] = 1 << 30
+    os.environ["PA_DEBUG_VALIDATE"] = "0"
+    try:
+        got = out_to_f64(run_decode(pk, case, 1, 64, 4, "f16", out_dtype="f32", partition_tokens=8))
+    finally:
+        os.environ["PA_DEBUG_VALIDATE"] = "1"
+    assert np.all(np.isnan(got[1]))
+    assert np.max(np.abs(got[[0, 2]] - want[[0, 2]])) <= TOL["f16"]
+
+
+def test_decode_empty_batch_and_argument_errors(gpu):
+    import torch
+    pk = gpu
+    pool = pk.Pool(4, 16, 2, 128, "f16")
+    q = torch.zeros((0, 2, 128), dtype=torch.float16, device="cuda")
+    out = pk.decode(pool, q, torch.zeros((0, 1), dtype=torch.int32, device="cuda"),
+                    torch.zeros((0,), dtype=torch.int32, device="cuda"), 0)
+    assert out.shape == (0, 2, 128)
+    q = torch.zeros((1, 6, 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(pk.PaError) as e:                     # group 3 is not instantiated
+        pk.decode(pool, q, torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
+                  torch.ones((1,), dtype=torch.int32, device="cuda"), 1)
+    assert e.value.code == -2
+    with pytest.raises(pk.PaError):                          # partition not a multiple of block_size
+        pk.decode(pool, torch.zeros((1, 2, 128), dtype=torch.float16, device="cuda"),
+                  torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
+                  torch.ones((1,), dtype=torch.int32, device="cuda"), 1, partition_tokens=24)
