@@ -1,0 +1,387 @@
+"""Throughput of the paged decode hot path on one MI355X.
+
+One timed step is one decode step of a batch of sequences through every
+attention layer of a model slice:
+
+1. the host block manager appends one token to each sequence
+   (``pa_bm_step``: new block or copy-on-write pair, slot mapping, padded
+   block tables and lengths, written into pinned host memory);
+2. the metadata goes to the device (async copies on the stream);
+3. per layer: ``pa_copy_blocks`` (if the step made copy-on-write pairs),
+   ``pa_write_kv`` of the new token's K/V, ``pa_decode`` over every cached
+   token.
+
+Each layer has its own KV pool (same block tables, as in a model), so
+consecutive decodes never re-read KV that the previous one left in the
+256 MB Infinity Cache or the L2s.  All inputs are seeded synthetic values of
+the workload's shape, resident in HBM before timing starts.
+
+Printed: one JSON line.  ``value`` is KV bytes read by decode per second of
+the whole timed region (host step, copies and kernels included);
+``roofline`` is the decode call alone, timed with HIP events on its stream;
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
+workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--layers L] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_355_amd", "csrc", "decode_impl.h")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=4, help="attention layers per step, one KV pool each")
+    ap.add_argument("--workload", default="mha7b_fp16")
+    ap.add_argument("--partition-tokens", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the steps, run a plain elementwise copy of this many MiB three times "
+                         "(calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# state
+# ----------------------------------------------------------------------------
+def build_state(pk, w, sc, layers, steps_total):
+    """Block manager with the workload's state, L seeded KV pools and the inputs."""
+    import numpy as np
+    import torch
+    from workloads import device_fill_, seed_for
+
+    bm = pk.BlockManager(sc.num_blocks, w.block_size, sc.free_order)
+    for op in sc.all_ops():
+        if op[0] == "add":
+            bm.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            bm.fork(op[1], op[2])
+        else:
+            bm.step(op[1])
+    ids = np.asarray(sc.measured, dtype=np.int64)
+    B = ids.shape[0]
+    max_before = max(sc.lengths_before[s] for s in sc.measured)
+    stride = -(-(max_before + steps_total) // w.block_size)
+    seed = seed_for(w)
+    tdt = pk.torch_dtype(w.dtype)
+    pools, q, k_new, v_new, out = [], [], [], [], []
+    for layer in range(layers):
+        pool = pk.Pool(sc.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype)
+        base = seed + 100 * layer
+        device_fill_(pool.k, base + 1, w.value_scale)
+        device_fill_(pool.v, base + 2, w.value_scale)
+        pools.append(pool)
+        k_new.append(device_fill_(torch.empty((B, w.kv_heads, w.head_dim), dtype=tdt, device="cuda"), base + 3,
+                                  w.value_scale))
+        v_new.append(device_fill_(torch.empty_like(k_new[-1]), base + 4, w.value_scale))
+        q.append(device_fill_(torch.empty((B, w.q_heads, w.head_dim), dtype=tdt, device="cuda"), base + 5,
+                              w.value_scale))
+        out.append(torch.empty((B, w.q_heads, w.head_dim), dtype=tdt, device="cuda"))
+    return dict(bm=bm, ids=ids, B=B, stride=stride, pools=pools, q=q, k_new=k_new, v_new=v_new, out=out)
+
+
+class HostBuffers:
+    """Pinned metadata written by the block manager; reused once its copy has left."""
+
+    def __init__(self, B, stride):
+        import torch
+        self.slots = torch.empty(B, dtype=torch.int32, pin_memory=True)
+        self.pairs = torch.empty((B, 2), dtype=torch.int32, pin_memory=True)
+        self.tables = torch.empty((B, stride), dtype=torch.int32, pin_memory=True)
+        self.lens = torch.empty(B, dtype=torch.int32, pin_memory=True)
+        self.lens_np = self.lens.numpy()
+        self.copied = None   # event recorded after the copies out of these buffers
+
+
+# ----------------------------------------------------------------------------
+# the timed step
+# ----------------------------------------------------------------------------
+def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
+    """n_steps decode steps; returns per-step KV bytes read by decode."""
+    import torch
+    from paged_kv_cache_355_amd._lib import lib, check
+
+    L = lib()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    B, stride = st["B"], st["stride"]
+    ids_ptr = st["ids"].ctypes.data
+    row_bytes = 2 * w.kv_heads * w.head_dim * pk.api.ELEM_BYTES[w.dtype]   # K + V per token
+    kv_bytes = []
+    for i in range(n_steps):
+        hb = hbufs[(step0 + i) % len(hbufs)]
+        if hb.copied is not None:
+            hb.copied.synchronize()
+        n_cow = st["bm"].step_into(ids_ptr, B, hb.slots.data_ptr(), hb.pairs.data_ptr(), hb.tables.data_ptr(),
+                                   stride, hb.lens.data_ptr())
+        max_len = int(hb.lens_np.max())
+        dev["tables"].copy_(hb.tables, non_blocking=True)
+        dev["lens"].copy_(hb.lens, non_blocking=True)
+        dev["slots"].copy_(hb.slots, non_blocking=True)
+        if n_cow:
+            dev["pairs"][:n_cow].copy_(hb.pairs[:n_cow], non_blocking=True)
+        if hb.copied is None:
+            hb.copied = torch.cuda.Event()
+        hb.copied.record(stream)
+        ws = dev["workspace"]
+        ws_bytes = ws.numel()
+        for layer, pool in enumerate(st["pools"]):
+            if n_cow:
+                check(L.pa_copy_blocks(pool.handle, dev["pairs"].data_ptr(), n_cow, sptr), "pa_copy_blocks")
+            check(L.pa_write_kv(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
+                                dev["slots"].data_ptr(), B, sptr), "pa_write_kv")
+            if timing is not None:
+                ev0, ev1 = timing["free"].pop()
+                ev0.record(stream)
+            check(L.pa_decode(pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype],
+                              st["q"][layer].data_ptr(), B, w.q_heads, dev["tables"].data_ptr(), stride,
+                              dev["lens"].data_ptr(), max_len, 0.0, partition_tokens, ws.data_ptr(), ws_bytes,
+                              sptr), "pa_decode")
+            if timing is not None:
+                ev1.record(stream)
+                timing["used"].append((ev0, ev1))
+        kv_bytes.append(int(hb.lens_np.astype("int64").sum()) * row_bytes * len(st["pools"]))
+    return kv_bytes
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle sample
+# ----------------------------------------------------------------------------
+def cpu_baseline(w, sc, budget_s):
+    """The oracle's full step (block manager, KV write, fp64 decode) for one layer of
+    the same batch, repeated while the time budget lasts (at least once)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle.attention import paged_decode
+    from oracle.block_manager import OracleBlockManager
+    from oracle.kv_ops import write_kv as oracle_write_kv, copy_blocks as oracle_copy_blocks
+    from oracle.numerics import bits_dtype, elem_bytes
+
+    ora = OracleBlockManager(sc.num_blocks, w.block_size, sc.free_order)
+    for op in sc.all_ops():
+        if op[0] == "add":
+            ora.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            ora.fork(op[1], op[2])
+        else:
+            ora.step(op[1])
+    ids = list(sc.measured)
+    rng = np.random.default_rng(12345)
+    bt = bits_dtype(w.dtype)
+    shape = (sc.num_blocks, w.kv_heads, w.block_size, w.head_dim)
+    # finite small values in every block (bit patterns of |x| < 1); values do not change the oracle's cost
+    limit = 0x3F800000 if w.dtype == "f32" else (0x3C00 if w.dtype == "f16" else 0x3F80)
+    k_pool = np.zeros(shape, dtype=bt)
+    v_pool = np.zeros(shape, dtype=bt)
+    used = np.array(sorted({b for s in ids for b in ora.block_table(s)[0]}), dtype=np.int64)
+    tile = rng.integers(0, limit, size=(256,) + shape[1:], dtype=bt)
+    k_pool[used] = tile[np.arange(used.shape[0]) % 256]
+    v_pool[used] = tile[(np.arange(used.shape[0]) + 128) % 256]
+    q = rng.integers(0, limit, size=(len(ids), w.q_heads, w.head_dim), dtype=bt)
+    k_new = rng.integers(0, limit, size=(len(ids), w.kv_heads, w.head_dim), dtype=bt)
+    v_new = rng.integers(0, limit, size=(len(ids), w.kv_heads, w.head_dim), dtype=bt)
+    row_bytes = 2 * w.kv_heads * w.head_dim * elem_bytes(w.dtype)
+    times, kv = [], []
+    with threadpool_limits(limits=1):
+        t_start = time.perf_counter()
+        while not times or (time.perf_counter() - t_start < budget_s and len(times) < 3):
+            t0 = time.perf_counter()
+            slots, pairs = ora.step(ids)
+            oracle_copy_blocks(k_pool, v_pool, pairs)
+            oracle_write_kv(k_pool, v_pool, k_new, v_new, slots)
+            lens = np.array([ora.length(s) for s in ids], dtype=np.int64)
+            stride = -(-int(lens.max()) // w.block_size)
+            tables = np.array(ora.padded_tables(ids, stride, pad=0), dtype=np.int32)
+            paged_decode(q, k_pool, v_pool, tables, lens, w.dtype)
+            times.append(time.perf_counter() - t0)
+            kv.append(int(lens.sum()) * row_bytes)
+    t = sum(times)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(sum(kv) / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(times)} full decode step(s) of the {len(ids)}-sequence batch through one layer "
+                  f"(block manager step, KV write, fp64 paged decode), single-threaded numpy",
+        "seq_steps_per_s": round(len(ids) * len(times) / t, 3),
+        "seconds": round(t, 3),
+        "host_cpu": cpu_model,
+        "host_cpus_available": os.cpu_count(),
+    }
+
+
+# ----------------------------------------------------------------------------
+# HBM traffic recorded from rocprofv3 counters for this kernel source
+# ----------------------------------------------------------------------------
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per decode call from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{"):
+            rec = json.loads(line)
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def copy_probe(mib):
+    """A plain elementwise kernel of known traffic (reads and writes mib MiB)."""
+    import torch
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 x torch.neg over {mib} MiB fp16 (reads {mib} MiB, writes {mib} MiB per dispatch)")
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode path shards by sequence or kv-head with no exchange; run one process per GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import paged_kv_cache_355_amd as pk
+    from workloads import WORKLOADS, make_scenario
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pk.lib()
+    w = WORKLOADS[args.workload]
+    sc = make_scenario(w)
+    steps_total = args.warmup + args.steps
+    log(f"[bench] workload {w.name}: B={len(sc.measured)} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} "
+        f"{w.dtype} bs={w.block_size} pool={sc.num_blocks} blocks x {args.layers} layers")
+    st = build_state(pk, w, sc, args.layers, steps_total)
+    B = st["B"]
+    part = args.partition_tokens or w.partition_tokens
+    max_ctx_bound = st["stride"] * w.block_size
+    dev = {
+        "tables": torch.empty((B, st["stride"]), dtype=torch.int32, device="cuda"),
+        "lens": torch.empty(B, dtype=torch.int32, device="cuda"),
+        "slots": torch.empty(B, dtype=torch.int32, device="cuda"),
+        "pairs": torch.empty((B, 2), dtype=torch.int32, device="cuda"),
+    }
+    ws_bytes = pk.decode_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
+    dev["workspace"] = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    resolved_part = pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
+    hbufs = [HostBuffers(B, st["stride"]) for _ in range(2)]
+    torch.cuda.synchronize()
+    log(f"[bench] state ready; warmup {args.warmup} steps")
+
+    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    timing = {"used": [], "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                   for _ in range(args.steps * args.layers)]}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kv_bytes = run_steps(pk, w, st, args.steps, part, dev, hbufs, args.warmup, timing)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in timing["used"]]
+    log(f"[bench] done: {elapsed * 1e3:.2f} ms for {args.steps} steps")
+
+    total_kv = sum(kv_bytes)
+    per_call_bytes = total_kv / len(dec_ms)
+    mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
+    achieved = per_call_bytes / mean_dec_s / 1e9
+    value = total_kv / elapsed / 1e9
+    layers = len(st["pools"])
+    traffic = recorded_traffic(w.name)
+    dec_sorted = sorted(dec_ms)
+    result = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + seq-steps/s, 7B shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "pool_blocks": sc.num_blocks,
+            "layers_per_step": layers, "partition_tokens": resolved_part,
+            "context_lens": "uniform [128, 2048] before the first warmup step, +1 per step"
+            if w.name == "mha7b_fp16" else w.notes,
+            "mean_context_len_timed": round(total_kv / (args.steps * layers * 2 * w.kv_heads * w.head_dim *
+                                                        pk.api.ELEM_BYTES[w.dtype]) / B, 1),
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "seq_steps_per_s_per_layer": round(B * layers * args.steps / elapsed, 1),
+        "decode_call_us": {"mean": round(mean_dec_s * 1e6, 2),
+                           "p10": round(dec_sorted[len(dec_sorted) // 10] * 1e3, 2),
+                           "p50": round(dec_sorted[len(dec_sorted) // 2] * 1e3, 2),
+                           "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2)},
+        "roofline": {
+            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_call": int(per_call_bytes),
+        },
+        "cpu_baseline": None,
+    }
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle sample (budget {args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, sc, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
