@@ -133,14 +133,18 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* s
 /* Paged decode attention ([P2] §1.1, §3.2.2 step 4, §4.1, §4.2)            */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of device workspace pa_decode needs for these sizes (0 when every
- * sequence fits one partition).  partition_tokens as for pa_decode. */
+/* Bytes of device workspace pa_decode needs for these sizes (0 when no
+ * partial results are kept).  partition_tokens as for pa_decode.  With the
+ * balanced split (partition_tokens 0) the size depends on the current
+ * device's CU count and occupancy, so ask on the device that will decode.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
 pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
                                     int32_t max_context_len, int32_t partition_tokens,
                                     int64_t* bytes);
 
-/* The partition length pa_decode will use for these sizes (resolves 0 =
- * automatic). */
+/* The partition length pa_decode will use for these sizes: partition_tokens
+ * itself, the PA_PARTITION_TOKENS override when partition_tokens is 0, or 0
+ * for the balanced split. */
 pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
                                      int32_t max_context_len, int32_t partition_tokens,
                                      int32_t* resolved);
@@ -157,13 +161,26 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
  *     valid block ids; block_table_stride ≥ ceil(max_context_len/block_size).
  *   context_lens: device int32[num_seqs], each in [0, max_context_len];
  *     a length of 0 gives a zero row.  Slots past the length are never used.
- *   max_context_len: host-known bound that sizes the launch grid.
+ *   max_context_len: host-known bound that sizes the launch.
  *   scale: the logit scale; ≤ 0 selects 1/sqrt(head_dim).
- *   partition_tokens: tokens per work partition (split-K over the context);
- *     0 = automatic, else a positive multiple of block_size.  Sequences
- *     longer than one partition are combined by a second reduce kernel.
- *   workspace: device memory of ≥ pa_decode_workspace_bytes(...) bytes
- *     (fp32 partial max/sum/output per partition); may be NULL when that is 0.
+ *   partition_tokens: how the context is split into work ([P2] §4.1's tiled
+ *     softmax, merged with running max and sum):
+ *       0 — the balanced split: one grid of workgroups, all resident at
+ *           once, each taking an equal share of the batch's total KV; pieces
+ *           of a sequence that straddle workgroups are merged inside the
+ *           same kernel (no second launch);
+ *       > 0 — fixed partitions of that many tokens (a multiple of
+ *           block_size), one workgroup each, merged by a second reduce kernel.
+ *     With 0, PA_PARTITION_TOKENS (if set and positive) selects fixed
+ *     partitions instead.
+ *   workspace: device memory of ≥ pa_decode_workspace_bytes(...) bytes,
+ *     256-byte aligned; may be NULL when that is 0.  The balanced split keeps
+ *     merge counters at the end of the workspace_bytes it is given: a new
+ *     workspace must be zero-filled once before its first use, and every call
+ *     leaves the counters at zero again, so the workspace can be reused by
+ *     later calls on the same pool with the same q_heads and any sizes up to
+ *     those it was sized for.  Calls that may run concurrently need separate
+ *     workspaces.
  * A length above max_context_len, or a block id outside the pool, yields NaN
  * in that sequence's output rows instead of a memory access out of bounds.
  * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */

@@ -103,6 +103,7 @@ def copy_blocks(pool, pairs, stream=None):
 
 
 def decode_workspace_bytes(pool, num_seqs, q_heads, max_context_len, partition_tokens=0):
+    """Workspace bytes ``decode`` needs; a new workspace must be zero-filled once before use."""
     out = ctypes.c_int64()
     check(lib().pa_decode_workspace_bytes(pool.handle, num_seqs, q_heads, max_context_len, partition_tokens,
                                           ctypes.addressof(out)), "pa_decode_workspace_bytes")
@@ -110,6 +111,7 @@ def decode_workspace_bytes(pool, num_seqs, q_heads, max_context_len, partition_t
 
 
 def decode_partition_tokens(pool, num_seqs, q_heads, max_context_len, partition_tokens=0):
+    """Partition length ``decode`` will use (0 = the balanced split)."""
     out = ctypes.c_int32()
     check(lib().pa_decode_partition_tokens(pool.handle, num_seqs, q_heads, max_context_len, partition_tokens,
                                            ctypes.addressof(out)), "pa_decode_partition_tokens")
@@ -129,7 +131,7 @@ def decode(pool, q, block_tables, context_lens, max_context_len, out=None, out_d
         out = torch.empty((num_seqs, q_heads, d), dtype=torch_dtype(odt), device=q.device)
     ws_bytes = decode_workspace_bytes(pool, num_seqs, q_heads, max_context_len, partition_tokens)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)   # merge counters start at zero
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stride = int(block_tables.shape[1]) if block_tables.dim() == 2 else 0

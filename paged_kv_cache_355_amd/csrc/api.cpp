@@ -78,23 +78,65 @@ pa_status fetch_ints(const int32_t* dev, int64_t n, std::vector<int32_t>* host, 
   return PA_OK;
 }
 
-// Partition length for a decode of these sizes: an explicit multiple of the
-// block size, the PA_PARTITION_TOKENS override, or 512 tokens.
-pa_status resolve_partition(const pa_pool* pool, int32_t requested, int32_t* out) {
-  int32_t p = requested > 0 ? requested : env_int("PA_PARTITION_TOKENS", 512);
-  if (p <= 0 || p % pool->d.block_size != 0) {
-    return fail(PA_ERR_INVALID, "partition_tokens must be a positive multiple of block_size (" +
-                                    std::to_string(pool->d.block_size) + ")");
-  }
-  *out = p;
-  return PA_OK;
-}
+// How pa_decode splits the work for these sizes, and where its workspace
+// pieces sit.
+struct DecodePlan {
+  bool balanced = false;
+  int32_t partition_tokens = 0;  // fixed partitions
+  int32_t max_parts = 1;
+  int32_t grid = 0;              // balanced split
+  int32_t num_slots = 0;
+  int64_t ml_off = 0, o_off = 0, counters_bytes = 0, bytes = 0;
+};
 
-int64_t workspace_for(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_parts) {
-  if (max_parts <= 1) return 0;
-  const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * max_parts;
-  const int64_t ml = ((rows * 2 * 4) + 255) / 256 * 256;
-  return ml + rows * pool->d.head_dim * 4;
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// An explicit positive partition length (a multiple of block_size), the
+// PA_PARTITION_TOKENS override, or (0) the balanced split.
+pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
+                      int32_t requested, DecodePlan* plan) {
+  const pa::PoolDesc& d = pool->d;
+  if (requested < 0) return fail(PA_ERR_INVALID, "partition_tokens must be >= 0");
+  const int32_t p = requested > 0 ? requested : env_int("PA_PARTITION_TOKENS", 0);
+  *plan = DecodePlan{};
+  if (p > 0) {
+    if (p % d.block_size != 0)
+      return fail(PA_ERR_INVALID, "partition_tokens must be a positive multiple of block_size (" +
+                                      std::to_string(d.block_size) + ")");
+    plan->partition_tokens = p;
+    plan->max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, p)));
+    if (plan->max_parts > 1) {
+      const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts;
+      plan->ml_off = 0;
+      plan->o_off = round256(rows * 2 * 4);
+      plan->bytes = plan->o_off + rows * d.head_dim * 4;
+    }
+    return PA_OK;
+  }
+  plan->balanced = true;
+  if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
+                                        " (q_heads must be kv_heads x 1, 2, 4 or 8)");
+  const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
+  if (units * std::max<int64_t>(max_context_len, 1) >= (int64_t{1} << 40))
+    return fail(PA_ERR_INVALID, "num_seqs * kv_heads * max_context_len must be < 2^40");
+  const int32_t group = q_heads / d.kv_heads;
+  int32_t grid = 0;
+  hipError_t e = pa::decode_balanced_grid(d, group, num_seqs, max_context_len, &grid);
+  if (e != hipSuccess) return hip_fail(e, "decode grid query");
+  if (units + grid >= (int64_t{1} << 31)) return fail(PA_ERR_INVALID, "too many sequences x kv-heads");
+  plan->grid = grid;
+  plan->num_slots = static_cast<int32_t>(units + grid);
+  const int64_t slots = plan->num_slots;
+  // Records from the front, merge counters against the end of the workspace
+  // the caller passes: a smaller call's counters then lie inside a larger
+  // call's counter area, never on its records, so one zero-filled workspace
+  // serves every call of one pool and q_heads up to the sizes it was made for.
+  plan->ml_off = 0;
+  plan->o_off = round256(slots * group * 2 * 4);
+  plan->counters_bytes = int64_t{pa::kMergeLevels} * slots * 4;
+  plan->bytes = plan->o_off + slots * group * d.head_dim * 4 + plan->counters_bytes;
+  return PA_OK;
 }
 
 }  // namespace
@@ -220,21 +262,27 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* s
 // ---------------------------------------------------------------------------
 pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
                                      int32_t partition_tokens, int32_t* resolved) {
-  (void)num_seqs;
-  (void)q_heads;
-  (void)max_context_len;
   if (!pool || !resolved) return fail(PA_ERR_INVALID, "NULL pointer");
-  return resolve_partition(pool, partition_tokens, resolved);
+  if (num_seqs < 0 || q_heads <= 0 || q_heads % pool->d.kv_heads != 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID, "bad sizes");
+  DecodePlan plan;
+  if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
+  *resolved = plan.balanced ? 0 : plan.partition_tokens;
+  return PA_OK;
 }
 
 pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
                                     int32_t partition_tokens, int64_t* bytes) {
   if (!pool || !bytes) return fail(PA_ERR_INVALID, "NULL pointer");
-  if (num_seqs < 0 || q_heads <= 0 || max_context_len < 0) return fail(PA_ERR_INVALID, "negative size");
-  int32_t P;
-  if (pa_status s = resolve_partition(pool, partition_tokens, &P)) return s;
-  const int32_t max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, P)));
-  *bytes = workspace_for(pool, num_seqs, q_heads, max_parts);
+  if (num_seqs < 0 || q_heads <= 0 || q_heads % pool->d.kv_heads != 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID, "bad sizes");
+  DecodePlan plan;
+  if (num_seqs == 0) {
+    *bytes = 0;
+    return PA_OK;
+  }
+  if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
+  *bytes = plan.bytes;
   return PA_OK;
 }
 
@@ -259,12 +307,11 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
   if (block_table_stride < ceil_div(max_context_len, d.block_size))
     return fail(PA_ERR_INVALID, "block_table_stride shorter than ceil(max_context_len / block_size)");
   if (!aligned(q, 16)) return fail(PA_ERR_INVALID, "q must be 16-byte aligned");
-  int32_t P;
-  if (pa_status s = resolve_partition(pool, partition_tokens, &P)) return s;
-  const int32_t max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, P)));
-  const int64_t need = workspace_for(pool, num_seqs, q_heads, max_parts);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
-    return fail(PA_ERR_INVALID, "workspace must be 256-byte aligned and hold " + std::to_string(need) + " bytes");
+  DecodePlan plan;
+  if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
+    return fail(PA_ERR_INVALID,
+                "workspace must be 256-byte aligned and hold " + std::to_string(plan.bytes) + " bytes");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_validate()) {
     std::vector<int32_t> lens, tables;
@@ -282,6 +329,18 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
                                           std::to_string(b) + " outside the pool");
       }
     }
+    if (plan.balanced) {
+      std::vector<int32_t> ctr;
+      const int64_t n = int64_t{pa::kMergeLevels} * plan.num_slots;
+      const int64_t counters_off = (workspace_bytes & ~int64_t{3}) - plan.counters_bytes;
+      if (pa_status s = fetch_ints(reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
+                                                                    counters_off),
+                                   n, &ctr, st))
+        return s;
+      for (int64_t i = 0; i < n; ++i)
+        if (ctr[static_cast<size_t>(i)] != 0)
+          return fail(PA_ERR_INVALID, "workspace merge counters are not zero (zero-fill a new workspace once)");
+    }
   }
   pa::DecodeArgs a{};
   a.out = out;
@@ -295,12 +354,18 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
   a.max_context_len = max_context_len;
   const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d.head_dim));
   a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);  // log2(e)
-  a.partition_tokens = P;
-  a.max_parts = max_parts;
-  if (need > 0) {
-    const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * max_parts;
-    a.part_ml = static_cast<float*>(workspace);
-    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((rows * 2 * 4) + 255) / 256 * 256);
+  a.balanced = plan.balanced;
+  a.grid = plan.grid;
+  a.num_slots = plan.num_slots;
+  a.partition_tokens = plan.partition_tokens;
+  a.max_parts = plan.max_parts;
+  if (plan.bytes > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.counters = plan.balanced
+                     ? reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~int64_t{3}) - plan.counters_bytes)
+                     : nullptr;
+    a.part_ml = reinterpret_cast<float*>(ws + plan.ml_off);
+    a.part_o = reinterpret_cast<float*>(ws + plan.o_off);
   }
   hipError_t e = pa::launch_decode(d, a, st);
   return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");

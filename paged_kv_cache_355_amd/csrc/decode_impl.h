@@ -1,6 +1,6 @@
-// Paged single-query decode attention for gfx950 (CDNA4), split-K over the
-// context.  Included by decode_<dtype>.hip, one translation unit per storage
-// type so the instantiations compile in parallel.
+// Paged single-query decode attention for gfx950 (CDNA4).  Included by
+// decode_<dtype>.hip, one translation unit per storage type so the
+// instantiations compile in parallel.
 //
 // What is computed ([P2] "PagedAttention：操作系统级 KV 缓存虚拟内存管理"):
 //   §1.1   out = softmax(q·Kᵀ·scale)·V, one query row per head;
@@ -11,29 +11,39 @@
 //   §4.2   each block is contiguous, so it is read with wide vector loads.
 //
 // Mapping onto gfx950:
-//   * Work unit = (sequence, kv-head, partition of P tokens).  One workgroup of
-//     NW wave64s per unit; the G = q_heads/kv_heads query rows of the kv-head
-//     stay in registers, so K and V of the unit are read from HBM exactly once.
+//   * The G = q_heads/kv_heads query rows of one kv-head are processed
+//     together and stay in registers, so K and V are read from HBM once per
+//     kv-head.
 //   * A token row (head_dim elements) is spread over LPT lanes with 16 bytes
 //     per lane, so one wave-wide global_load_dwordx4 moves 1 KiB: TPL = 64/LPT
 //     consecutive tokens of one contiguous (block, kv-head) tile.
 //   * Each LPT-lane group keeps its own running max/sum/output for the tokens
 //     it loads, so the hot loop needs no cross-group traffic: scores are
 //     reduced inside the group with DPP row rotations fused into v_add
-//     (v_dot2 for fp16/bf16 products), groups and waves are merged once per
-//     unit at the end.
-//   * Loads of the next block are issued before the current block is consumed
-//     (two register buffers), keeping ~2 KiB per lane-group of K/V in flight.
-//   * Softmax runs in base 2: scores carry scale·log2(e) and v_exp_f32 does
-//     2^x.
-//   * A unit that holds a whole sequence writes the normalised output; longer
-//     sequences write fp32 (max, sum, unnormalised output) per partition and
-//     decode_reduce_kernel merges them.
+//     (v_dot2 for fp16/bf16 products); groups and waves are merged once per
+//     piece of work at the end.
+//   * Loads of the next chunk are issued before the current chunk is consumed
+//     (two register buffers).
+//   * Softmax runs in base 2: scores carry scale·log2(e) and v_exp_f32 does 2^x.
+//
+// Two ways of dealing out the work (both exact up to fp32 rounding order):
+//   * Balanced (the default): the (sequence, kv-head) units are laid end to
+//     end on one axis of CT-token chunks and every workgroup of a single,
+//     fully resident grid takes an equal slice of that axis.  Units cut by a
+//     slice boundary produce partial (max, sum, output) records that the last
+//     arriving piece merges, through a fan-in-16 tree for long units, so no
+//     second kernel runs and every CU finishes at the same time whatever the
+//     length mix.
+//   * Fixed partitions (an explicit partition length): one workgroup per
+//     (sequence, kv-head, partition of P tokens) and a second kernel,
+//     decode_reduce_kernel, merges the partitions of longer sequences.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <type_traits>
 
 #include "launch.h"
 
@@ -41,6 +51,12 @@ namespace pa {
 namespace dec {
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so 2^(m - m') never sees inf - inf
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kFanIn = 16;      // records merged per node of the balanced kernel's merge tree
+constexpr int kMaxLevels = 3;   // kFanIn^3 = 4096 ≥ pieces of any unit (≤ grid + 1)
+static_assert(kMaxBalancedGrid + 1 <= kFanIn * kFanIn * kFanIn, "merge tree too shallow for the largest grid");
+constexpr int kSeqsPerThread = 8;
 
 template <int DT>
 struct Elem;
@@ -137,6 +153,8 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ float qnan() { return __uint_as_float(0x7fc00000u); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
@@ -164,58 +182,75 @@ struct Shape {
   static_assert(LPT == 8 || LPT == 16 || LPT == 32, "unsupported head_dim / dtype pair");
 };
 
-// ---------------------------------------------------------------------------
-// decode_partition_kernel
-//   grid  = (max_parts, kv_heads, num_seqs), block = NW × 64 threads
-//   Unit (s, g, p) covers tokens [p·P, min((p+1)·P, len_s)) of sequence s,
-//   kv-head g, and the G query heads g·G … g·G+G-1.
-// ---------------------------------------------------------------------------
-template <int DT, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
-    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
-    void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
-    const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
-    int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
-    float scale_log2) {
-  using S = Shape<DT, D>;
-  constexpr int ELEMS = S::ELEMS, LPT = S::LPT, TPL = S::TPL, ROW = S::ROW;
-  // A chunk is NLC wave-wide loads per tensor.  Blocks of ≥ TPL tokens: four
-  // loads (TPL-token groups never straddle a block, as both are powers of
-  // two).  Smaller blocks: one load whose lane groups find their own blocks.
-  constexpr bool kSmallBlocks = BS < TPL;
-  constexpr int NLC = kSmallBlocks ? 1 : 4;
-  constexpr int CT = NLC * TPL;              // tokens per chunk
-  constexpr int64_t TILE = static_cast<int64_t>(BS) * ROW;
+// A chunk is NLC wave-wide loads per tensor.  Blocks of ≥ TPL tokens: four
+// loads (TPL-token groups never straddle a block, as both are powers of two).
+// Smaller blocks: one load whose lane groups find their own blocks.
+template <int DT, int D, int BS>
+struct Chunk {
+  static constexpr bool kSmallBlocks = BS < Shape<DT, D>::TPL;
+  static constexpr int NLC = kSmallBlocks ? 1 : 4;
+  static constexpr int CT = NLC * Shape<DT, D>::TPL;   // tokens per chunk
+};
 
-  const int p = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+// LDS of one workgroup: the block ids of the range being read, staged once
+// per batch, and the buffers through which the NW waves merge their results.
+constexpr int kTableBatch = 512;   // block ids staged per batch (a multiple of every CT / BS)
+
+template <int NW, int G, int D>
+struct WaveMerge {
+  float o[NW][G][D];
+  float m[NW][G];
+  float l[NW][G];
+  int bad[NW];
+  int32_t tbl[kTableBatch];   // physical block ids, -1 for an id outside the pool
+};
+
+// ---------------------------------------------------------------------------
+// attend_range: the G query rows of kv-head g of sequence s over tokens
+// [t_begin, t_end), t_begin < t_end, t_begin a multiple of CT or (fixed
+// partitions) of block_size.  Chunks of CT tokens are dealt to the NW waves
+// round-robin.  Every thread then calls emit(r, d, M, L, O, bad) for its share
+// of the G×D outputs: M is the running max (base 2), L = Σ 2^(score−M),
+// O = Σ 2^(score−M)·v[d] for query row r, and bad reports a block id outside
+// the pool (then the values are meaningless).  Ends with a barrier, so the
+// caller may call it again.
+//
+// Memory-level parallelism: every wave keeps the next chunk's 2·NLC loads in
+// flight while it consumes the current one.  The loads are issued
+// unconditionally (a load past the range reads this lane's 16 bytes of q,
+// which are valid and cache-resident) and padding values are masked after
+// unpacking, never by writing to the load registers, so the wait before each
+// chunk is a fixed "all but the last 2·NLC loads" rather than a full drain.
+// Block ids come from LDS, staged kTableBatch at a time, so no global load of
+// the table sits between two chunks.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int BS, int G, int NW, typename Emit>
+__device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+                                             const char* __restrict__ q, const int32_t* __restrict__ table,
+                                             int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
+                                             int32_t t_begin, int32_t t_end, float scale_log2,
+                                             WaveMerge<NW, G, D>& sh, Emit&& emit) {
+  using S = Shape<DT, D>;
+  using CK = Chunk<DT, D, BS>;
+  constexpr int ELEMS = S::ELEMS, LPT = S::LPT, TPL = S::TPL, ROW = S::ROW;
+  constexpr bool kSmallBlocks = CK::kSmallBlocks;
+  constexpr int NLC = CK::NLC, CT = CK::CT;
+  constexpr int64_t TILE = static_cast<int64_t>(BS) * ROW;
+  static_assert(kTableBatch % (CT > BS ? CT / BS : 1) == 0, "table batches must hold whole chunks");
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int q_heads = kv_heads * G;
-
-  const int32_t len = context_lens[s];
-  const bool bad_len = len < 0 || len > max_ctx;
-  const int32_t len_c = bad_len ? 0 : len;
-  const int32_t nparts = len_c <= part_tokens ? 1 : (len_c + part_tokens - 1) / part_tokens;
-  if (p >= nparts) return;
-
-  const int32_t t_begin = p * part_tokens;
-  const int32_t t_end = min(t_begin + part_tokens, len_c);
-  const int32_t nchunks = (t_end - t_begin + CT - 1) / CT;
-  const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
 
   const int grp = lane / LPT;     // which token of a wave-wide load this lane reads
   const int sub = lane % LPT;     // which 16-byte slice of the row
   const int32_t lane_off = grp * ROW + sub * 16;
 
   // query rows of this kv-head: 16 bytes per lane per row
+  const char* q_lane = q + ((static_cast<int64_t>(s) * q_heads + g * G) * D) * S::EB + sub * 16;
   uint4 qv[G];
 #pragma unroll
-  for (int r = 0; r < G; ++r) {
-    const int h = g * G + r;
-    qv[r] = *reinterpret_cast<const uint4*>(q + ((static_cast<int64_t>(s) * q_heads + h) * D) * S::EB + sub * 16);
-  }
+  for (int r = 0; r < G; ++r) qv[r] = *reinterpret_cast<const uint4*>(q_lane + r * D * S::EB);
 
   float m[G], l[G], o[G][ELEMS];
 #pragma unroll
@@ -227,103 +262,127 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
   }
   bool bad_block = false;
 
-  auto lookup = [&](int32_t t) {
-    int32_t phys = table[t / BS];
-    if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(num_blocks)) {
-      bad_block = true;
-      phys = 0;
+  const int32_t blk_first = t_begin / BS;
+  const int32_t blk_last = (t_end - 1) / BS;
+  for (int32_t bb = blk_first; bb <= blk_last; bb += kTableBatch) {
+    const int32_t nb = min(kTableBatch, blk_last - bb + 1);
+    __syncthreads();   // the previous batch's ids are no longer read
+    for (int i = threadIdx.x; i < nb; i += NW * 64) {
+      const int32_t phys = table[bb + i];
+      sh.tbl[i] = static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks) ? phys : -1;
     }
-    return (static_cast<int64_t>(phys) * kv_heads + g) * TILE;
-  };
+    __syncthreads();
+    const int32_t tb = max(t_begin, bb * BS);
+    const int32_t te = min(t_end, (bb + nb) * BS);
+    const int32_t nchunks = (te - tb + CT - 1) / CT;
 
-  // Issue the loads of chunk c (K and V, NLC wave-wide 16-byte loads each).
-  // Every address stays inside an allocated block; padding slots past the
-  // context may be read but their lanes are masked before use.
-  auto load_chunk = [&](int32_t c, uint4 (&kb)[NLC], uint4 (&vb)[NLC]) {
-    const int32_t tok0 = t_begin + c * CT;
-    if constexpr (!kSmallBlocks) {
-      if constexpr (BS >= CT) {
-        const int64_t tile = lookup(tok0) + (tok0 % BS) * ROW;
-        const char* kt = k_pool + tile;
-        const char* vt = v_pool + tile;
+    // Byte offset of token t's row in its (block, kv-head) tile; t lies in this batch.
+    auto tile_of = [&](int32_t t) {
+      int32_t phys = sh.tbl[t / BS - bb];
+      if (phys < 0) {
+        bad_block = true;
+        phys = 0;
+      }
+      return (static_cast<int64_t>(phys) * kv_heads + g) * TILE + (t % BS) * ROW;
+    };
+
+    // Issue the loads of chunk c (K and V, NLC wave-wide 16-byte loads each).
+    // live = false: the chunk lies past the range; read q instead.  Padding
+    // slots past t_end inside an allocated block may be read; their lanes are
+    // masked before use.
+    auto load_chunk = [&](int32_t c, bool live, uint4 (&kb)[NLC], uint4 (&vb)[NLC]) {
+      const int32_t tok0 = tb + (live ? c : 0) * CT;
+      if constexpr (!kSmallBlocks) {
+        if constexpr (BS >= CT) {
+          // a chunk never straddles a block: tb is a multiple of CT here
+          const int64_t tile = tile_of(tok0) + lane_off;
 #pragma unroll
-        for (int i = 0; i < NLC; ++i) {
-          kb[i] = *reinterpret_cast<const uint4*>(kt + lane_off + i * TPL * ROW);
-          vb[i] = *reinterpret_cast<const uint4*>(vt + lane_off + i * TPL * ROW);
+          for (int i = 0; i < NLC; ++i) {
+            kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile + i * TPL * ROW : q_lane);
+            vb[i] = *reinterpret_cast<const uint4*>(live ? v_pool + tile + i * TPL * ROW : q_lane);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NLC; ++i) {
+            // a load starting past the range end re-reads the chunk's first
+            // group (always inside an allocated block); its lanes are masked
+            const int32_t t = tok0 + i * TPL < te ? tok0 + i * TPL : tok0;
+            const int64_t tile = tile_of(t) + lane_off;
+            kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile : q_lane);
+            vb[i] = *reinterpret_cast<const uint4*>(live ? v_pool + tile : q_lane);
+          }
         }
       } else {
+        int32_t t = tok0 + grp;
+        if (t >= te) t = te - 1;
+        const int64_t off = tile_of(t) + sub * 16;
+        kb[0] = *reinterpret_cast<const uint4*>(live ? k_pool + off : q_lane);
+        vb[0] = *reinterpret_cast<const uint4*>(live ? v_pool + off : q_lane);
+      }
+    };
+
+    // Fold chunk c into the running (m, l, o) of this lane group.
+    auto consume_chunk = [&](int32_t c, const uint4 (&kb)[NLC], const uint4 (&vb)[NLC]) {
+      const int32_t tok0 = tb + c * CT;
+      const bool full = tok0 + CT <= te;   // wave-uniform
+      bool valid[NLC];
+#pragma unroll
+      for (int i = 0; i < NLC; ++i) valid[i] = full || (tok0 + grp + i * TPL < te);
+      float vf[NLC][ELEMS];
+#pragma unroll
+      for (int i = 0; i < NLC; ++i) unpack<DT>(vb[i], vf[i]);
+      if (!full) {
+        // padding may hold NaN or Inf: zero it, since 0·NaN would poison the sum
 #pragma unroll
         for (int i = 0; i < NLC; ++i) {
-          // a load starting past the partition end re-reads the chunk's first
-          // group (always inside an allocated block); its lanes are masked
-          const int32_t t = tok0 + i * TPL < t_end ? tok0 + i * TPL : tok0;
-          const int64_t tile = lookup(t) + (t % BS) * ROW;
-          kb[i] = *reinterpret_cast<const uint4*>(k_pool + tile + lane_off);
-          vb[i] = *reinterpret_cast<const uint4*>(v_pool + tile + lane_off);
+#pragma unroll
+          for (int e = 0; e < ELEMS; ++e) vf[i][e] = valid[i] ? vf[i][e] : 0.f;
         }
       }
-    } else {
-      int32_t t = tok0 + grp;
-      if (t >= t_end) t = t_end - 1;
-      const int64_t off = lookup(t) + (t % BS) * ROW + sub * 16;
-      kb[0] = *reinterpret_cast<const uint4*>(k_pool + off);
-      vb[0] = *reinterpret_cast<const uint4*>(v_pool + off);
-    }
-  };
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        float sc[NLC];
+        float mx = kNegBig;
+#pragma unroll
+        for (int i = 0; i < NLC; ++i) {
+          sc[i] = group_sum<LPT>(dot16<DT>(qv[r], kb[i])) * scale_log2;
+          if (valid[i]) mx = fmaxf(mx, sc[i]);
+        }
+        const float m_new = fmaxf(m[r], mx);
+        const float alpha = exp2f_fast(m[r] - m_new);
+        float psum = 0.f;
+        float pi[NLC];
+#pragma unroll
+        for (int i = 0; i < NLC; ++i) {
+          pi[i] = valid[i] ? exp2f_fast(sc[i] - m_new) : 0.f;
+          psum += pi[i];
+        }
+        l[r] = l[r] * alpha + psum;
+#pragma unroll
+        for (int e = 0; e < ELEMS; ++e) {
+          float acc = o[r][e] * alpha;
+#pragma unroll
+          for (int i = 0; i < NLC; ++i) acc = __builtin_fmaf(pi[i], vf[i][e], acc);
+          o[r][e] = acc;
+        }
+        m[r] = m_new;
+      }
+    };
 
-  // Fold chunk c into the running (m, l, o) of this lane group.
-  auto consume_chunk = [&](int32_t c, uint4 (&kb)[NLC], uint4 (&vb)[NLC]) {
-    const int32_t tok0 = t_begin + c * CT;
-    const bool full = tok0 + CT <= t_end;
-    bool valid[NLC];
-#pragma unroll
-    for (int i = 0; i < NLC; ++i) {
-      valid[i] = full || (tok0 + grp + i * TPL < t_end);
-      if (!valid[i]) vb[i] = make_uint4(0u, 0u, 0u, 0u);  // padding may hold NaN: never multiply it
-    }
-    float vf[NLC][ELEMS];
-#pragma unroll
-    for (int i = 0; i < NLC; ++i) unpack<DT>(vb[i], vf[i]);
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      float sc[NLC];
-      float mx = kNegBig;
-#pragma unroll
-      for (int i = 0; i < NLC; ++i) {
-        sc[i] = group_sum<LPT>(dot16<DT>(qv[r], kb[i])) * scale_log2;
-        if (valid[i]) mx = fmaxf(mx, sc[i]);
-      }
-      const float m_new = fmaxf(m[r], mx);
-      const float alpha = exp2f_fast(m[r] - m_new);
-      float psum = 0.f;
-      float pi[NLC];
-#pragma unroll
-      for (int i = 0; i < NLC; ++i) {
-        pi[i] = valid[i] ? exp2f_fast(sc[i] - m_new) : 0.f;
-        psum += pi[i];
-      }
-      l[r] = l[r] * alpha + psum;
-#pragma unroll
-      for (int e = 0; e < ELEMS; ++e) {
-        float acc = o[r][e] * alpha;
-#pragma unroll
-        for (int i = 0; i < NLC; ++i) acc = __builtin_fmaf(pi[i], vf[i][e], acc);
-        o[r][e] = acc;
-      }
-      m[r] = m_new;
-    }
-  };
-
-  // Chunks wave, wave+NW, wave+2NW, … with the next chunk's loads in flight.
-  {
+    // Chunks wave, wave+NW, wave+2NW, … with the next chunk's loads in flight.
+    // (The scheduling barriers keep the compiler from hoisting the current
+    // chunk's arithmetic above the next chunk's load issue, which would make
+    // the wave wait for its data before the prefetch leaves.)
     uint4 ka[NLC], va[NLC], kb2[NLC], vb2[NLC];
     int32_t c = wave;
-    if (c < nchunks) load_chunk(c, ka, va);
+    load_chunk(c, c < nchunks, ka, va);
     for (; c < nchunks; c += 2 * NW) {
-      if (c + NW < nchunks) load_chunk(c + NW, kb2, vb2);
+      load_chunk(c + NW, c + NW < nchunks, kb2, vb2);
+      __builtin_amdgcn_sched_barrier(0);
       consume_chunk(c, ka, va);
       if (c + NW >= nchunks) break;
-      if (c + 2 * NW < nchunks) load_chunk(c + 2 * NW, ka, va);
+      load_chunk(c + 2 * NW, c + 2 * NW < nchunks, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
       consume_chunk(c + NW, kb2, vb2);
     }
   }
@@ -348,59 +407,101 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
     }
   }
 
-  // Merge the NW waves through LDS and write the unit's result.
-  __shared__ float sh_o[NW][G][D];
-  __shared__ float sh_m[NW][G];
-  __shared__ float sh_l[NW][G];
-  __shared__ int sh_bad[NW];
+  // Merge the NW waves through LDS and hand each output to emit.
   if (lane < LPT) {
 #pragma unroll
     for (int r = 0; r < G; ++r) {
 #pragma unroll
-      for (int e = 0; e < ELEMS; ++e) sh_o[wave][r][sub * ELEMS + e] = o[r][e];
+      for (int e = 0; e < ELEMS; ++e) sh.o[wave][r][sub * ELEMS + e] = o[r][e];
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      sh_m[wave][r] = m[r];
-      sh_l[wave][r] = l[r];
+      sh.m[wave][r] = m[r];
+      sh.l[wave][r] = l[r];
     }
   }
   const bool wave_bad = __any(bad_block);
-  if (lane == 0) sh_bad[wave] = wave_bad ? 1 : 0;
+  if (lane == 0) sh.bad[wave] = wave_bad ? 1 : 0;
   __syncthreads();
-  bool bad = bad_len;
+  bool bad = false;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) bad = bad || sh_bad[w] != 0;
-  const float nan = __uint_as_float(0x7fc00000u);
+  for (int w = 0; w < NW; ++w) bad = bad || sh.bad[w] != 0;
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int r = idx / D;
     const int d = idx - r * D;
     float mm = kNegBig;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sh_m[w][r]);
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sh.m[w][r]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float a = exp2f_fast(sh_m[w][r] - mm);
-      L += sh_l[w][r] * a;
-      O += sh_o[w][r][d] * a;
+      const float a = exp2f_fast(sh.m[w][r] - mm);
+      L += sh.l[w][r] * a;
+      O += sh.o[w][r][d] * a;
     }
-    const int h = g * G + r;
-    const int64_t row = static_cast<int64_t>(s) * q_heads + h;
-    if (nparts == 1) {
-      const float x = bad ? nan : (L > 0.f ? O / L : 0.f);
-      store_out(out, out_dtype, row * D + d, x);
-    } else {
-      const int64_t prow = row * max_parts + p;
-      part_o[prow * D + d] = bad ? nan : O;
-      if (d == 0) {
-        part_ml[2 * prow] = mm;
-        part_ml[2 * prow + 1] = L;
-      }
-    }
+    emit(r, d, mm, L, O, bad);
   }
+  __syncthreads();
+}
+
+// Write zero rows (an empty context) or NaN rows (an invalid length) for all
+// query heads of kv-head range [g0, g1) of sequence s.
+template <int D, int G>
+__device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t s, int32_t q_heads, int32_t g0,
+                                          int32_t g1, float value) {
+  const int64_t first = (static_cast<int64_t>(s) * q_heads + g0 * G) * D;
+  const int32_t n = (g1 - g0) * G * D;
+  for (int32_t i = threadIdx.x; i < n; i += blockDim.x) store_out(out, out_dtype, first + i, value);
+}
+
+// ---------------------------------------------------------------------------
+// decode_partition_kernel (fixed partitions)
+//   grid  = (max_parts, kv_heads, num_seqs), block = NW × 64 threads
+//   Unit (s, g, p) covers tokens [p·P, min((p+1)·P, len_s)) of sequence s,
+//   kv-head g, and the G query heads g·G … g·G+G-1.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
+    void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
+    const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
+    int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
+    float scale_log2) {
+  const int p = blockIdx.x;
+  const int g = blockIdx.y;
+  const int s = blockIdx.z;
+  const int q_heads = kv_heads * G;
+
+  const int32_t len = context_lens[s];
+  const bool bad_len = len < 0 || len > max_ctx;
+  const int32_t len_c = bad_len ? 0 : len;
+  const int32_t nparts = len_c <= part_tokens ? 1 : (len_c + part_tokens - 1) / part_tokens;
+  if (p >= nparts) return;
+  if (len_c == 0) {
+    fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
+    return;
+  }
+  const int32_t t_begin = p * part_tokens;
+  const int32_t t_end = min(t_begin + part_tokens, len_c);
+  const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
+  __shared__ WaveMerge<NW, G, D> sh;
+  attend_range<DT, D, BS, G, NW>(
+      k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
+      [&](int r, int d, float M, float L, float O, bool bad) {
+        const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
+        if (nparts == 1) {
+          store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
+        } else {
+          const int64_t prow = row * max_parts + p;
+          part_o[prow * D + d] = bad ? qnan() : O;
+          if (d == 0) {
+            part_ml[2 * prow] = M;
+            part_ml[2 * prow + 1] = L;
+          }
+        }
+      });
 }
 
 // ---------------------------------------------------------------------------
@@ -461,17 +562,339 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(void* __restrict__ o
     float O = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) O += sh_red[k * 32 + dl];
-    const float x = bad_len ? __uint_as_float(0x7fc00000u) : (L > 0.f ? O / L : 0.f);
+    const float x = bad_len ? qnan() : (L > 0.f ? O / L : 0.f);
     store_out(out, out_dtype, row * D + d, x);
   }
 }
 
-constexpr int kWaves = 4;
+// ---------------------------------------------------------------------------
+// Balanced split (the default)
+// ---------------------------------------------------------------------------
+
+// Chunks of CT tokens a sequence of length len contributes per kv-head
+// (0 for an empty or invalid length).
+template <int CT>
+__device__ __forceinline__ int64_t seq_chunks(int32_t len, int32_t max_ctx) {
+  return (len <= 0 || len > max_ctx) ? 0 : (static_cast<int64_t>(len) + CT - 1) / CT;
+}
+
+// Exclusive prefix sum of v over the block's threads; *total gets the sum.
+template <int NW>
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* total, int64_t* sh /*[NW]*/) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int64_t before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int64_t t = sh[w];
+    if (w < wave) before += t;
+    sum += t;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + x - v;
+}
+
+// Slice boundary of workgroup w when C chunks are split over W workgroups:
+// floor(w·C / W), computed without overflow for C < 2^40.
+__device__ __forceinline__ int64_t slice_start(int64_t w, int64_t C, int64_t W) {
+  return w * (C / W) + (w * (C % W)) / W;
+}
+
+// The workgroup whose slice holds chunk x: the largest w with slice_start(w) ≤ x.
+__device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t C, int64_t W) {
+  return ((x + 1) * W - 1) / C;
+}
+
+// Partial records pass between workgroups that may sit on different XCDs,
+// whose L2 caches are not kept coherent with each other.  They are stored and
+// loaded as device-scope relaxed atomics, which go to the coherent level of
+// the memory hierarchy, so no device-wide fence (an L2 write-back or
+// invalidate) is needed: a writer's stores have completed once its workgroup
+// passes the barrier before the counter increment, and a reader issues its
+// loads only after the increment that tells it it is last.
+__device__ __forceinline__ void st_rec(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_rec(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge records child 0 … nchild-1 (slots slot0 + c·span) into either the
+// final output rows of unit (s, g) or a record at slot0.  All threads call it.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_records(float* __restrict__ rec_ml, float* __restrict__ rec_o, int64_t slot0,
+                                              int64_t span, int32_t nchild, bool final_out, void* __restrict__ out,
+                                              int32_t out_dtype, int32_t s, int32_t g, int32_t q_heads) {
+  __shared__ float sh_scale[G][kFanIn];
+  __shared__ float sh_ML[G][2];
+  const int tid = threadIdx.x;
+  if (tid < G) {
+    const int r = tid;
+    float M = kNegBig;
+    float mc[kFanIn], lc[kFanIn];
+    for (int c = 0; c < nchild; ++c) {
+      const int64_t rr = (slot0 + c * span) * G + r;
+      mc[c] = ld_rec(rec_ml + rr * 2);
+      lc[c] = ld_rec(rec_ml + rr * 2 + 1);
+      M = fmaxf(M, mc[c]);
+    }
+    float L = 0.f;
+    for (int c = 0; c < nchild; ++c) {
+      const float a = exp2f_fast(mc[c] - M);
+      sh_scale[r][c] = a;
+      L += lc[c] * a;   // a NaN sum marks a piece that met a bad block id
+    }
+    sh_ML[r][0] = M;
+    sh_ML[r][1] = L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += NW * 64) {
+    const int r = idx / D;
+    const int d = idx - r * D;
+    float O = 0.f;
+    for (int c = 0; c < nchild; ++c) O += sh_scale[r][c] * ld_rec(rec_o + ((slot0 + c * span) * G + r) * D + d);
+    if (final_out) {
+      const float L = sh_ML[r][1];
+      const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
+      store_out(out, out_dtype, row * D + d, L > 0.f ? O / L : (L != L ? qnan() : 0.f));
+    } else {
+      st_rec(rec_o + (slot0 * G + r) * D + d, O);   // same thread read this element of child 0 above
+    }
+  }
+  __syncthreads();   // every read of child 0's (max, sum) is done
+  if (!final_out && tid < G) {
+    st_rec(rec_ml + (slot0 * G + tid) * 2, sh_ML[tid][0]);
+    st_rec(rec_ml + (slot0 * G + tid) * 2 + 1, sh_ML[tid][1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode_balanced_kernel
+//   grid = W workgroups (all resident at once), block = NW × 64 threads.
+//   Unit u = s·kv_heads + g owns c_s = ceil(len_s / CT) consecutive chunks of
+//   a global axis of C = kv_heads·Σ c_s chunks; workgroup w processes chunks
+//   [floor(wC/W), floor((w+1)C/W)).  A unit cut by slice boundaries yields
+//   one piece per workgroup it touches; piece k of unit u writes a record at
+//   slot u + first_owner(u) + k (slots are distinct because both u and w only
+//   grow along the axis).  Records merge up a fan-in-kFanIn tree: a node's
+//   counter (ctr[level][slot of its first record]) counts finished children,
+//   the last child to arrive merges them (or writes the output at the root)
+//   and resets the counter to zero for the next call.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
+    void* __restrict__ out, int32_t out_dtype, int32_t* __restrict__ ctr, float* __restrict__ rec_ml,
+    float* __restrict__ rec_o, const int32_t* __restrict__ block_tables, int32_t table_stride,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_blocks, int32_t kv_heads,
+    int32_t max_ctx, int32_t num_slots, float scale_log2) {
+  constexpr int NT = NW * 64;
+  constexpr int CT = Chunk<DT, D, BS>::CT;
+  const int64_t w = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t q_heads = kv_heads * G;
+
+  // Rows of empty or invalid sequences, spread over the grid.
+  for (int64_t s = w; s < num_seqs; s += gridDim.x) {
+    const int32_t len = context_lens[s];
+    if (len <= 0 || len > max_ctx) {
+      fill_rows<D, G>(out, out_dtype, static_cast<int32_t>(s), q_heads, 0, kv_heads, len == 0 ? 0.f : qnan());
+    }
+  }
+
+  // Total chunks.  Each thread covers kSeqsPerThread consecutive sequences per
+  // round; their lengths are loaded together (clamped indices, no branches),
+  // so the loads overlap instead of waiting one by one.
+  __shared__ int64_t sh_scan[NW];
+  __shared__ int64_t sh_found[2];
+  constexpr int64_t kPerRound = static_cast<int64_t>(NT) * kSeqsPerThread;
+  auto thread_chunks = [&](int64_t round_base, int64_t (&ck)[kSeqsPerThread]) {
+    int32_t lk[kSeqsPerThread];
+#pragma unroll
+    for (int k = 0; k < kSeqsPerThread; ++k) {
+      const int64_t sq = round_base + static_cast<int64_t>(tid) * kSeqsPerThread + k;
+      lk[k] = context_lens[sq < num_seqs ? sq : num_seqs - 1];
+    }
+    int64_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < kSeqsPerThread; ++k) {
+      const int64_t sq = round_base + static_cast<int64_t>(tid) * kSeqsPerThread + k;
+      ck[k] = sq < num_seqs ? seq_chunks<CT>(lk[k], max_ctx) : 0;
+      mine += ck[k];
+    }
+    return mine;
+  };
+  int64_t total = 0;
+  for (int64_t base = 0; base < num_seqs; base += kPerRound) {
+    int64_t ck[kSeqsPerThread];
+    int64_t round_total;
+    block_exclusive_scan<NW>(thread_chunks(base, ck), &round_total, sh_scan);
+    total += round_total;
+  }
+  const int64_t C = total * kv_heads;
+  // Workgroups past the chunk count sit out, so every slice holds at least one
+  // chunk and a unit's pieces are exactly the workgroups its chunks span.
+  const int64_t W = min(static_cast<int64_t>(gridDim.x), C);
+  if (w >= W) return;
+  const int64_t start = slice_start(w, C, W);
+  const int64_t end = slice_start(w + 1, C, W);
+  if (start >= end) return;
+
+  // Locate the sequence holding chunk `start` and the chunks before it.
+  if (tid == 0) sh_found[0] = -1;
+  __syncthreads();
+  int64_t run = 0;
+  for (int64_t base = 0; base < num_seqs; base += kPerRound) {
+    int64_t ck[kSeqsPerThread];
+    const int64_t mine = thread_chunks(base, ck);
+    int64_t round_total;
+    const int64_t excl = block_exclusive_scan<NW>(mine, &round_total, sh_scan);
+    const int64_t lo = (run + excl) * kv_heads;
+    const int64_t hi = (run + excl + mine) * kv_heads;
+    if (lo <= start && start < hi) {   // exactly one thread
+      int64_t P = run + excl;
+      for (int k = 0; k < kSeqsPerThread; ++k) {
+        if ((P + ck[k]) * kv_heads > start) {
+          sh_found[0] = base + static_cast<int64_t>(tid) * kSeqsPerThread + k;
+          sh_found[1] = P;
+          break;
+        }
+        P += ck[k];
+      }
+    }
+    run += round_total;
+    __syncthreads();
+    if (sh_found[0] >= 0) break;
+  }
+
+  // Walk the units that meet [start, end).
+  int32_t s = static_cast<int32_t>(sh_found[0]);
+  int64_t P = sh_found[1];
+  __shared__ int sh_last;
+  __shared__ WaveMerge<NW, G, D> sh;
+  for (; s < num_seqs; ++s) {
+    const int32_t len = context_lens[s];
+    const int64_t c = seq_chunks<CT>(len, max_ctx);
+    const int64_t base = P * kv_heads;
+    if (base >= end) break;
+    P += c;
+    if (c == 0) continue;
+    const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
+    for (int32_t g = start > base ? static_cast<int32_t>((start - base) / c) : 0; g < kv_heads; ++g) {
+      const int64_t off = base + g * c;
+      if (off >= end) break;
+      const int64_t a = max(start, off) - off;
+      const int64_t b = min(end, off + c) - off;
+      const int32_t t0 = static_cast<int32_t>(a * CT);
+      const int32_t t1 = static_cast<int32_t>(min(b * CT, static_cast<int64_t>(len)));
+      if (a == 0 && b == c) {   // the whole unit: write the output directly
+        attend_range<DT, D, BS, G, NW>(
+            k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
+            [&](int r, int d, float M, float L, float O, bool bad) {
+              const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
+              store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
+            });
+        continue;
+      }
+      const int64_t u = static_cast<int64_t>(s) * kv_heads + g;
+      const int64_t first_w = slice_owner(off, C, W);
+      const int64_t slot0 = u + first_w;
+      int32_t n = static_cast<int32_t>(slice_owner(off + c - 1, C, W) - first_w + 1);   // pieces
+      int32_t idx = static_cast<int32_t>(w - first_w);
+      const int64_t my_slot = slot0 + idx;
+      attend_range<DT, D, BS, G, NW>(
+          k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
+          [&](int r, int d, float M, float L, float O, bool bad) {
+            const int64_t rr = my_slot * G + r;
+            st_rec(rec_o + rr * D + d, O);
+            if (d == 0) {
+              st_rec(rec_ml + rr * 2, M);
+              st_rec(rec_ml + rr * 2 + 1, bad ? qnan() : L);
+            }
+          });
+      // Climb the merge tree while this workgroup is the last child to finish.
+      int64_t span = 1;
+      for (int level = 0; level < kMaxLevels; ++level) {
+        const int32_t parent = idx / kFanIn;
+        const int32_t nchild = min(kFanIn, n - parent * kFanIn);
+        const int64_t pslot = slot0 + static_cast<int64_t>(parent) * kFanIn * span;
+        int32_t* counter = ctr + static_cast<int64_t>(level) * num_slots + pslot;
+        __syncthreads();   // every wave's record stores have completed (the barrier waits on them)
+        if (tid == 0) sh_last = atomicAdd(counter, 1) == nchild - 1;
+        __syncthreads();
+        if (!sh_last) break;
+        if (tid == 0) atomicExch(counter, 0);
+        const int32_t n_up = (n + kFanIn - 1) / kFanIn;
+        merge_records<D, G, NW>(rec_ml, rec_o, pslot, span, nchild, n_up == 1, out, out_dtype, s, g, q_heads);
+        if (n_up == 1) break;
+        idx = parent;
+        n = n_up;
+        span *= kFanIn;
+      }
+      __syncthreads();   // sh_last is read by every thread before the next piece rewrites it
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch
+// ---------------------------------------------------------------------------
+
+// Workgroups of the balanced kernel: every one resident at once (occupancy ×
+// CUs), at most one per chunk the batch can hold, or PA_DECODE_GRID.
+template <int DT, int D, int BS, int G>
+hipError_t balanced_grid(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
+  constexpr int CT = Chunk<DT, D, BS>::CT;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static int cached[64];   // resident workgroups per device, 0 = not yet asked
+  int resident = dev >= 0 && dev < 64 ? cached[dev] : 0;
+  if (resident == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_balanced_kernel<DT, D, BS, G, kWaves>, kThreads,
+                                                     0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    resident = per_cu * cus;
+    if (resident <= 0) resident = cus > 0 ? cus : 1;
+    if (dev >= 0 && dev < 64) cached[dev] = resident;
+  }
+  int64_t W = resident;
+  if (const char* v = std::getenv("PA_DECODE_GRID")) {
+    const long x = std::strtol(v, nullptr, 10);
+    if (x > 0) W = x;
+  }
+  const int64_t bound = static_cast<int64_t>(num_seqs) * p.kv_heads * ((static_cast<int64_t>(max_ctx) + CT - 1) / CT);
+  if (W > bound) W = bound;
+  if (W > kMaxBalancedGrid) W = kMaxBalancedGrid;
+  if (W < 1) W = 1;
+  *grid = static_cast<int32_t>(W);
+  return hipSuccess;
+}
 
 template <int DT, int D, int BS, int G>
 hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
+  if (a.balanced) {
+    hipLaunchKernelGGL((decode_balanced_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
+                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
+                       a.out, a.out_dtype, a.counters, a.part_ml, a.part_o, a.block_tables, a.table_stride,
+                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.num_slots,
+                       a.scale_log2);
+    return hipGetLastError();
+  }
   dim3 grid(a.max_parts, p.kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kWaves * 64), 0, stream,
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
                      a.table_stride, a.context_lens, p.num_blocks, p.kv_heads, a.max_context_len, a.max_parts,
@@ -484,36 +907,59 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   return hipGetLastError();
 }
 
-template <int DT, int D, int BS>
-hipError_t launch_group(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
-  switch (a.q_heads / p.kv_heads) {
-    case 1: return launch_typed<DT, D, BS, 1>(p, a, stream);
-    case 2: return launch_typed<DT, D, BS, 2>(p, a, stream);
-    case 4: return launch_typed<DT, D, BS, 4>(p, a, stream);
-    case 8: return launch_typed<DT, D, BS, 8>(p, a, stream);
+// Dispatch on (head_dim, block_size, group) to Fn<DT, D, BS, G>::run(args...).
+template <int DT, template <int, int, int, int> class Fn, typename... Args>
+hipError_t dispatch(const PoolDesc& p, int32_t group, Args&&... args) {
+  auto by_group = [&](auto d_tag, auto bs_tag) -> hipError_t {
+    constexpr int D = decltype(d_tag)::value;
+    constexpr int BS = decltype(bs_tag)::value;
+    switch (group) {
+      case 1: return Fn<DT, D, BS, 1>::run(p, args...);
+      case 2: return Fn<DT, D, BS, 2>::run(p, args...);
+      case 4: return Fn<DT, D, BS, 4>::run(p, args...);
+      case 8: return Fn<DT, D, BS, 8>::run(p, args...);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  auto by_bs = [&](auto d_tag) -> hipError_t {
+    switch (p.block_size) {
+      case 4: return by_group(d_tag, std::integral_constant<int, 4>{});
+      case 8: return by_group(d_tag, std::integral_constant<int, 8>{});
+      case 16: return by_group(d_tag, std::integral_constant<int, 16>{});
+      case 32: return by_group(d_tag, std::integral_constant<int, 32>{});
+      case 64: return by_group(d_tag, std::integral_constant<int, 64>{});
+      default: return hipErrorInvalidValue;
+    }
+  };
+  switch (p.head_dim) {
+    case 64: return by_bs(std::integral_constant<int, 64>{});
+    case 128: return by_bs(std::integral_constant<int, 128>{});
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int DT, int D>
-hipError_t launch_bs(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
-  switch (p.block_size) {
-    case 4: return launch_group<DT, D, 4>(p, a, stream);
-    case 8: return launch_group<DT, D, 8>(p, a, stream);
-    case 16: return launch_group<DT, D, 16>(p, a, stream);
-    case 32: return launch_group<DT, D, 32>(p, a, stream);
-    case 64: return launch_group<DT, D, 64>(p, a, stream);
-    default: return hipErrorInvalidValue;
+template <int DT, int D, int BS, int G>
+struct LaunchFn {
+  static hipError_t run(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
+    return launch_typed<DT, D, BS, G>(p, a, stream);
   }
-}
+};
+
+template <int DT, int D, int BS, int G>
+struct GridFn {
+  static hipError_t run(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
+    return balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, grid);
+  }
+};
 
 template <int DT>
 hipError_t launch_dtype(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
-  switch (p.head_dim) {
-    case 64: return launch_bs<DT, 64>(p, a, stream);
-    case 128: return launch_bs<DT, 128>(p, a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch<DT, LaunchFn>(p, a.q_heads / p.kv_heads, a, stream);
+}
+
+template <int DT>
+hipError_t grid_dtype(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
+  return dispatch<DT, GridFn>(p, group, num_seqs, max_ctx, grid);
 }
 
 }  // namespace dec

@@ -11,6 +11,13 @@ enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 inline int32_t elem_bytes(int32_t dt) { return dt == kF32 ? 4 : 2; }
 
+// Largest grid of the balanced decode kernel (its merge tree holds at most
+// 16^3 records per unit, and a unit meets at most grid + 1 workgroups).
+constexpr int32_t kMaxBalancedGrid = 4095;
+// Levels of the balanced kernel's merge tree (one int32 counter per record
+// slot per level).
+constexpr int32_t kMergeLevels = 3;
+
 struct PoolDesc {
   int32_t num_blocks, block_size, kv_heads, head_dim, dtype;
   void* k;
@@ -28,10 +35,19 @@ struct DecodeArgs {
   const int32_t* context_lens;
   int32_t max_context_len;
   float scale_log2;        // logit scale × log2(e)
+  // Balanced split (balanced = true): one resident grid of `grid` workgroups
+  // sharing the work evenly; partial records live in num_slots slots.
+  bool balanced;
+  int32_t grid;
+  int32_t num_slots;       // num_seqs * kv_heads + grid
+  int32_t* counters;       // [kMergeLevels][num_slots], zero on entry and exit
+  // Fixed partitions (balanced = false).
   int32_t partition_tokens;
   int32_t max_parts;       // partitions covering max_context_len
-  float* part_ml;          // [num_seqs][q_heads][max_parts][2]   (max, sum)
-  float* part_o;           // [num_seqs][q_heads][max_parts][head_dim]
+  // Partial records.  Fixed partitions: [num_seqs][q_heads][max_parts] rows;
+  // balanced: [num_slots][group] rows.
+  float* part_ml;          // rows × (max, sum)
+  float* part_o;           // rows × head_dim
 };
 
 // True when the decode kernels are instantiated for these sizes.
@@ -42,9 +58,17 @@ hipError_t launch_write_kv(const PoolDesc& p, const void* k_new, const void* v_n
 hipError_t launch_copy_blocks(const PoolDesc& p, const int32_t* pairs, int32_t n, hipStream_t stream);
 hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 
-// Per-dtype decode launchers (decode_<dtype>.hip).
+// Workgroups of the balanced decode kernel for these sizes (every one
+// resident on the current device at once; PA_DECODE_GRID overrides).
+hipError_t decode_balanced_grid(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
+                                int32_t* grid);
+
+// Per-dtype decode launchers and grid queries (decode_<dtype>.hip).
 hipError_t launch_decode_f32(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
+hipError_t decode_grid_f32(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid);
+hipError_t decode_grid_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid);
+hipError_t decode_grid_bf16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid);
 
 }  // namespace pa

@@ -180,9 +180,10 @@ def test_decode_placement_invariance_is_bit_identical(gpu):
         case = dict(k_pool=k_pool, v_pool=v_pool, q=draw(rng, (3, 8, 128), "bf16", 1.0), num_blocks=nb,
                     tables=np.array(bm.padded_tables(range(3), 21, pad=-1), dtype=np.int32),
                     lens=np.array(lens, dtype=np.int32))
-        outs.append(run_decode(pk, case, 2, 128, 16, "bf16", out_dtype="f32", partition_tokens=64).cpu())
+        outs.append([run_decode(pk, case, 2, 128, 16, "bf16", out_dtype="f32", partition_tokens=p).cpu()
+                     for p in (64, 0)])
     for o in outs[1:]:
-        assert torch.equal(o, outs[0])
+        assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
 
 
 def test_decode_shared_prefix_matches_private_copy(gpu):
@@ -202,8 +203,64 @@ def test_decode_shared_prefix_matches_private_copy(gpu):
     case = dict(k_pool=k_pool, v_pool=v_pool, q=np.repeat(q1, 3, axis=0), num_blocks=64,
                 tables=np.array(bm.padded_tables([0, 1, 2], 7, pad=-1), dtype=np.int32),
                 lens=np.array([100, 100, 100], dtype=np.int32))
-    got = run_decode(pk, case, hkv, d, bs, "f16", out_dtype="f32").cpu()
+    # fixed partitions: the summation order depends only on logical positions → identical bits
+    got = run_decode(pk, case, hkv, d, bs, "f16", out_dtype="f32", partition_tokens=32).cpu()
     assert (got[0] == got[1]).all() and (got[0] == got[2]).all()
+    # balanced split: each sequence may be cut at other places, so equal up to fp32 rounding
+    got = out_to_f64(run_decode(pk, case, hkv, d, bs, "f16", out_dtype="f32"))
+    assert np.max(np.abs(got[0] - got[1])) <= 1e-6 and np.max(np.abs(got[0] - got[2])) <= 1e-6
+
+
+@pytest.mark.parametrize("grid", [1, 3, 37, 4000])
+def test_balanced_split_any_grid(gpu, grid):
+    """The balanced split is exact for any number of workgroups: one workgroup
+    walking every unit, a few that each cross many units, and more workgroups
+    than chunks, which cuts the longest sequence into ~300 pieces and merges
+    them through three levels of the fan-in-16 tree."""
+    pk = gpu
+    lens = [4999, 0, 3, 700, 31, 1]
+    case = build_case(lens, 1, 8, 128, 32, "bf16", 99, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "bf16")
+    os.environ["PA_DECODE_GRID"] = str(grid)
+    try:
+        got = out_to_f64(run_decode(pk, case, 1, 128, 32, "bf16", out_dtype="f32"))
+    finally:
+        del os.environ["PA_DECODE_GRID"]
+    assert np.all(got[1] == 0.0)
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
+
+
+def test_balanced_workspace_reuse_leaves_counters_zero(gpu):
+    """Three calls share one workspace (the second with fewer sequences); under
+    PA_DEBUG_VALIDATE each call first checks that the merge counters are zero."""
+    import torch
+    pk = gpu
+    case = build_case([900, 17, 2500, 64], 2, 4, 64, 16, "f16", 5, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
+    pool = pk.Pool(case["num_blocks"], 16, 2, 64, "f16", k=to_torch(case["k_pool"], "f16"),
+                   v=to_torch(case["v_pool"], "f16"))
+    q, tables, lens = to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(), \
+        torch.from_numpy(case["lens"]).cuda()
+    ws = torch.zeros(pk.decode_workspace_bytes(pool, 4, 8, 2500), dtype=torch.uint8, device="cuda")
+    for n in (4, 2, 4, 4):
+        out = pk.decode(pool, q[:n].contiguous(), tables[:n].contiguous(), lens[:n].contiguous(), 2500,
+                        out_dtype="f32", workspace=ws)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(out_to_f64(out) - want[:n])) <= TOL["f16"]
+
+
+def test_balanced_rejects_dirty_workspace_under_validation(gpu):
+    import torch
+    pk = gpu
+    case = build_case([300, 40], 1, 1, 128, 16, "f16", 8)
+    pool = pk.Pool(case["num_blocks"], 16, 1, 128, "f16", k=to_torch(case["k_pool"], "f16"),
+                   v=to_torch(case["v_pool"], "f16"))
+    ws = torch.zeros(pk.decode_workspace_bytes(pool, 2, 1, 300), dtype=torch.uint8, device="cuda")
+    ws[-1] = 1                                               # the merge counters sit at the end
+    with pytest.raises(pk.PaError) as e:
+        pk.decode(pool, to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(),
+                  torch.from_numpy(case["lens"]).cuda(), 300, workspace=ws)
+    assert "counters" in str(e.value)
 
 
 def test_decode_rejects_bad_metadata_under_validation(gpu):
@@ -222,18 +279,22 @@ def test_decode_rejects_bad_metadata_under_validation(gpu):
                   torch.from_numpy(case["lens"]).cuda(), 10)         # a length above max_context_len
 
 
-def test_decode_bad_table_entry_gives_nan_not_a_fault(gpu):
+@pytest.mark.parametrize("partition", [8, 0])
+def test_decode_bad_table_entry_gives_nan_not_a_fault(gpu, partition):
     """With host validation off, the kernel's own bounds check turns a block id
-    outside the pool into NaN output for that sequence only."""
+    outside the pool into NaN output for that sequence only (fixed partitions
+    and the balanced split, whose pieces carry the mark through the merge)."""
     pk = gpu
     case = build_case([20, 9, 30], 1, 1, 64, 4, "f16", 4)
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
     case["tables"][1, 1] = 1 << 30
     os.environ["PA_DEBUG_VALIDATE"] = "0"
+    os.environ["PA_DECODE_GRID"] = "5"
     try:
-        got = out_to_f64(run_decode(pk, case, 1, 64, 4, "f16", out_dtype="f32", partition_tokens=8))
+        got = out_to_f64(run_decode(pk, case, 1, 64, 4, "f16", out_dtype="f32", partition_tokens=partition))
     finally:
         os.environ["PA_DEBUG_VALIDATE"] = "1"
+        del os.environ["PA_DECODE_GRID"]
     assert np.all(np.isnan(got[1]))
     assert np.max(np.abs(got[[0, 2]] - want[[0, 2]])) <= TOL["f16"]
 
