@@ -53,8 +53,8 @@ def parse_args():
     ap.add_argument("--layers", type=int, default=4, help="attention layers per step, one KV pool each")
     ap.add_argument("--workload", default="mha7b_fp16")
     ap.add_argument("--partition-tokens", type=int, default=0,
-                    help="0 = the workload's setting (the balanced split unless it names fixed partitions); "
-                         "-1 = force the balanced split; > 0 = fixed partitions of that many tokens")
+                    help="0 = the workload's setting (the library's automatic choice unless it names fixed "
+                         "partitions); -1 = the balanced split; > 0 = fixed partitions of that many tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -300,7 +300,7 @@ def main():
         f"{w.dtype} bs={w.block_size} pool={sc.num_blocks} blocks x {args.layers} layers")
     st = build_state(pk, w, sc, args.layers, steps_total)
     B = st["B"]
-    part = w.partition_tokens if args.partition_tokens == 0 else max(args.partition_tokens, 0)
+    part = w.partition_tokens if args.partition_tokens == 0 else args.partition_tokens
     max_ctx_bound = st["stride"] * w.block_size
     dev = {
         "tables": torch.empty((B, st["stride"]), dtype=torch.int32, device="cuda"),
@@ -366,8 +366,10 @@ def main():
                            "p50": round(dec_sorted[len(dec_sorted) // 2] * 1e3, 2),
                            "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2)},
         "roofline": {
-            "kernel": ("pa_decode: decode_balanced_kernel" if resolved_part == 0 else
-                       "pa_decode: decode_partition_kernel + decode_reduce_kernel"),
+            "kernel": ("pa_decode: decode_balanced_kernel" if resolved_part < 0 else
+                       "pa_decode: decode_partition_kernel" + (" + decode_reduce_kernel"
+                                                               if resolved_part < max_ctx_bound else
+                                                               " (one workgroup per sequence and kv-head)")),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

@@ -134,17 +134,20 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* s
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace pa_decode needs for these sizes (0 when no
- * partial results are kept).  partition_tokens as for pa_decode.  With the
- * balanced split (partition_tokens 0) the size depends on the current
- * device's CU count and occupancy, so ask on the device that will decode.
+ * partial results are kept).  partition_tokens as for pa_decode.  The
+ * automatic choice and the balanced split depend on the current device's CU
+ * count and occupancy, so ask on the device that will decode.
  * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
 pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
                                     int32_t max_context_len, int32_t partition_tokens,
                                     int64_t* bytes);
 
-/* The partition length pa_decode will use for these sizes: partition_tokens
- * itself, the PA_PARTITION_TOKENS override when partition_tokens is 0, or 0
- * for the balanced split. */
+/* partition_tokens value that selects the balanced split (see pa_decode). */
+#define PA_PARTITION_BALANCED -1
+
+/* How pa_decode will split these sizes: the partition length in tokens (a
+ * length ≥ max_context_len means one workgroup per (sequence, kv-head)), or
+ * PA_PARTITION_BALANCED. */
 pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
                                      int32_t max_context_len, int32_t partition_tokens,
                                      int32_t* resolved);
@@ -165,14 +168,20 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
  *   scale: the logit scale; ≤ 0 selects 1/sqrt(head_dim).
  *   partition_tokens: how the context is split into work ([P2] §4.1's tiled
  *     softmax, merged with running max and sum):
- *       0 — the balanced split: one grid of workgroups, all resident at
+ *       > 0 — fixed partitions of that many tokens (a multiple of
+ *           block_size), one workgroup each, merged by a second reduce
+ *           kernel when a sequence has more than one;
+ *       PA_PARTITION_BALANCED — one grid of workgroups, all resident at
  *           once, each taking an equal share of the batch's total KV; pieces
  *           of a sequence that straddle workgroups are merged inside the
  *           same kernel (no second launch);
- *       > 0 — fixed partitions of that many tokens (a multiple of
- *           block_size), one workgroup each, merged by a second reduce kernel.
- *     With 0, PA_PARTITION_TOKENS (if set and positive) selects fixed
- *     partitions instead.
+ *       0 — automatic: PA_PARTITION_TOKENS if set and positive; else, when
+ *           the batch has at least as many (sequence, kv-head) units as the
+ *           device holds workgroups at once, one workgroup per unit with no
+ *           split; else the balanced split.
+ *     With fixed partitions and at most 256 sequences, the longest sequences
+ *     are dispatched first so the short ones fill the gaps at the end (the
+ *     results do not depend on the order).
  *   workspace: device memory of ≥ pa_decode_workspace_bytes(...) bytes,
  *     256-byte aligned; may be NULL when that is 0.  The balanced split keeps
  *     merge counters at the end of the workspace_bytes it is given: a new

@@ -5,9 +5,9 @@ manager, C ABI in include/pa.h); this package is its thin Python binding.
 The library is loaded on first use and its absence is an error: nothing here
 falls back to another implementation.
 """
-from ._lib import PaError, NoBlocksError, LIB_PATH, lib
+from ._lib import PaError, NoBlocksError, LIB_PATH, lib, PA_PARTITION_BALANCED
 from .api import (Pool, BlockManager, write_kv, copy_blocks, decode, decode_workspace_bytes,
                   decode_partition_tokens, torch_dtype, dtype_name)
 
-__all__ = ["PaError", "NoBlocksError", "LIB_PATH", "lib", "Pool", "BlockManager", "write_kv", "copy_blocks",
+__all__ = ["PaError", "NoBlocksError", "LIB_PATH", "lib", "PA_PARTITION_BALANCED", "Pool", "BlockManager", "write_kv", "copy_blocks",
            "decode", "decode_workspace_bytes", "decode_partition_tokens", "torch_dtype", "dtype_name"]

@@ -91,14 +91,30 @@ struct DecodePlan {
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// An explicit positive partition length (a multiple of block_size), the
-// PA_PARTITION_TOKENS override, or (0) the balanced split.
+// How to split: an explicit positive partition length (a multiple of
+// block_size) or PA_PARTITION_BALANCED; for 0, the PA_PARTITION_TOKENS
+// override, else whole sequences (one workgroup per (sequence, kv-head),
+// longest first) when the batch's units fill the device, else the balanced
+// split.
 pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
                       int32_t requested, DecodePlan* plan) {
   const pa::PoolDesc& d = pool->d;
-  if (requested < 0) return fail(PA_ERR_INVALID, "partition_tokens must be >= 0");
-  const int32_t p = requested > 0 ? requested : env_int("PA_PARTITION_TOKENS", 0);
+  if (requested < 0 && requested != PA_PARTITION_BALANCED)
+    return fail(PA_ERR_INVALID, "partition_tokens must be >= 0 or PA_PARTITION_BALANCED");
   *plan = DecodePlan{};
+  if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
+                                        " (q_heads must be kv_heads x 1, 2, 4 or 8)");
+  const int32_t group = q_heads / d.kv_heads;
+  const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
+  int32_t p = requested > 0 ? requested : (requested == 0 ? env_int("PA_PARTITION_TOKENS", 0) : 0);
+  int32_t grid = 0, capacity = 0;
+  if (p <= 0) {
+    hipError_t e = pa::decode_balanced_grid(d, group, num_seqs, max_context_len, &grid, &capacity);
+    if (e != hipSuccess) return hip_fail(e, "decode grid query");
+    if (requested == 0 && units >= capacity)   // whole sequences keep every CU busy
+      p = static_cast<int32_t>(ceil_div(std::max(max_context_len, 1), d.block_size) * d.block_size);
+  }
   if (p > 0) {
     if (p % d.block_size != 0)
       return fail(PA_ERR_INVALID, "partition_tokens must be a positive multiple of block_size (" +
@@ -114,16 +130,8 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
     return PA_OK;
   }
   plan->balanced = true;
-  if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
-    return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
-                                        " (q_heads must be kv_heads x 1, 2, 4 or 8)");
-  const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
   if (units * std::max<int64_t>(max_context_len, 1) >= (int64_t{1} << 40))
     return fail(PA_ERR_INVALID, "num_seqs * kv_heads * max_context_len must be < 2^40");
-  const int32_t group = q_heads / d.kv_heads;
-  int32_t grid = 0;
-  hipError_t e = pa::decode_balanced_grid(d, group, num_seqs, max_context_len, &grid);
-  if (e != hipSuccess) return hip_fail(e, "decode grid query");
   if (units + grid >= (int64_t{1} << 31)) return fail(PA_ERR_INVALID, "too many sequences x kv-heads");
   plan->grid = grid;
   plan->num_slots = static_cast<int32_t>(units + grid);
@@ -267,7 +275,7 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
     return fail(PA_ERR_INVALID, "bad sizes");
   DecodePlan plan;
   if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
-  *resolved = plan.balanced ? 0 : plan.partition_tokens;
+  *resolved = plan.balanced ? PA_PARTITION_BALANCED : plan.partition_tokens;
   return PA_OK;
 }
 

@@ -456,22 +456,56 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
   for (int32_t i = threadIdx.x; i < n; i += blockDim.x) store_out(out, out_dtype, first + i, value);
 }
 
+// Batches of at most this many sequences are dispatched longest first.
+constexpr int kRankMax = 256;
+
+// The sequence whose length ranks `rank` in decreasing order (ties by index;
+// empty and invalid lengths count as 0).  All threads call it; O(num_seqs)
+// LDS reads per thread.
+template <int NW>
+__device__ __forceinline__ int32_t seq_of_rank(int32_t rank, const int32_t* __restrict__ context_lens,
+                                               int32_t num_seqs, int32_t max_ctx) {
+  __shared__ int32_t sh_len[kRankMax];
+  __shared__ int32_t sh_seq;
+  for (int32_t i = threadIdx.x; i < num_seqs; i += NW * 64) {
+    const int32_t len = context_lens[i];
+    sh_len[i] = (len < 0 || len > max_ctx) ? 0 : len;
+  }
+  if (threadIdx.x == 0) sh_seq = rank;   // every rank is taken exactly once; this is only a default
+  __syncthreads();
+  for (int32_t t = threadIdx.x; t < num_seqs; t += NW * 64) {
+    const int32_t lt = sh_len[t];
+    int32_t r = 0;
+    for (int32_t u = 0; u < num_seqs; ++u) {
+      const int32_t lu = sh_len[u];
+      r += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+    }
+    if (r == rank) sh_seq = t;
+  }
+  __syncthreads();
+  return sh_seq;
+}
+
 // ---------------------------------------------------------------------------
 // decode_partition_kernel (fixed partitions)
 //   grid  = (max_parts, kv_heads, num_seqs), block = NW × 64 threads
 //   Unit (s, g, p) covers tokens [p·P, min((p+1)·P, len_s)) of sequence s,
-//   kv-head g, and the G query heads g·G … g·G+G-1.
+//   kv-head g, and the G query heads g·G … g·G+G-1.  With at most kRankMax
+//   sequences, blockIdx.z is a rank: the longest sequences are dispatched
+//   first and the short ones fill the gaps at the end (which workgroup
+//   computes a unit changes nothing in its result).
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BS, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
-    int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
+    int32_t num_seqs, int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
     float scale_log2) {
   const int p = blockIdx.x;
   const int g = blockIdx.y;
-  const int s = blockIdx.z;
+  const int s = num_seqs <= kRankMax ? seq_of_rank<NW>(blockIdx.z, context_lens, num_seqs, max_ctx)
+                                     : static_cast<int>(blockIdx.z);
   const int q_heads = kv_heads * G;
 
   const int32_t len = context_lens[s];
@@ -618,9 +652,14 @@ __device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t C, int64_t W) 
 // whose L2 caches are not kept coherent with each other.  They are stored and
 // loaded as device-scope relaxed atomics, which go to the coherent level of
 // the memory hierarchy, so no device-wide fence (an L2 write-back or
-// invalidate) is needed: a writer's stores have completed once its workgroup
-// passes the barrier before the counter increment, and a reader issues its
-// loads only after the increment that tells it it is last.
+// invalidate) is needed.  A writer waits until its own stores have completed
+// (wait_vmem) before the counter increment that publishes them, and a reader
+// issues its loads only after the increment that tells it it is last.  (A
+// workgroup-scope fence or barrier does not wait for global stores on this
+// target, so the wait is explicit.)
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited on
+}
 __device__ __forceinline__ void st_rec(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -828,7 +867,8 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
         const int32_t nchild = min(kFanIn, n - parent * kFanIn);
         const int64_t pslot = slot0 + static_cast<int64_t>(parent) * kFanIn * span;
         int32_t* counter = ctr + static_cast<int64_t>(level) * num_slots + pslot;
-        __syncthreads();   // every wave's record stores have completed (the barrier waits on them)
+        wait_vmem();       // this wave's record stores have completed …
+        __syncthreads();   // … and so have every other wave's
         if (tid == 0) sh_last = atomicAdd(counter, 1) == nchild - 1;
         __syncthreads();
         if (!sh_last) break;
@@ -851,6 +891,29 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
 
 // Workgroups of the balanced kernel: every one resident at once (occupancy ×
 // CUs), at most one per chunk the batch can hold, or PA_DECODE_GRID.
+// Workgroups of the fixed-partition kernel that fit on the current device at once.
+template <int DT, int D, int BS, int G>
+hipError_t partition_resident(int32_t* resident_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static int cached[64];
+  int resident = dev >= 0 && dev < 64 ? cached[dev] : 0;
+  if (resident == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partition_kernel<DT, D, BS, G, kWaves>,
+                                                     kThreads, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    resident = per_cu * cus;
+    if (resident <= 0) resident = cus > 0 ? cus : 1;
+    if (dev >= 0 && dev < 64) cached[dev] = resident;
+  }
+  *resident_out = resident;
+  return hipSuccess;
+}
+
 template <int DT, int D, int BS, int G>
 hipError_t balanced_grid(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
   constexpr int CT = Chunk<DT, D, BS>::CT;
@@ -897,8 +960,8 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
-                     a.table_stride, a.context_lens, p.num_blocks, p.kv_heads, a.max_context_len, a.max_parts,
-                     a.partition_tokens, a.scale_log2);
+                     a.table_stride, a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len,
+                     a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(D / 32, a.q_heads, a.num_seqs), dim3(256), 0, stream, a.out,
@@ -947,8 +1010,11 @@ struct LaunchFn {
 
 template <int DT, int D, int BS, int G>
 struct GridFn {
-  static hipError_t run(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
-    return balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, grid);
+  static hipError_t run(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
+                        int32_t* partition_capacity) {
+    hipError_t e = balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, grid);
+    if (e != hipSuccess) return e;
+    return partition_resident<DT, D, BS, G>(partition_capacity);
   }
 };
 
@@ -958,8 +1024,9 @@ hipError_t launch_dtype(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
 }
 
 template <int DT>
-hipError_t grid_dtype(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
-  return dispatch<DT, GridFn>(p, group, num_seqs, max_ctx, grid);
+hipError_t grid_dtype(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
+                      int32_t* partition_capacity) {
+  return dispatch<DT, GridFn>(p, group, num_seqs, max_ctx, grid, partition_capacity);
 }
 
 }  // namespace dec

@@ -100,11 +100,11 @@ hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t str
 }
 
 hipError_t decode_balanced_grid(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
-                                int32_t* grid) {
+                                int32_t* grid, int32_t* partition_capacity) {
   switch (p.dtype) {
-    case kF32: return decode_grid_f32(p, group, num_seqs, max_context_len, grid);
-    case kF16: return decode_grid_f16(p, group, num_seqs, max_context_len, grid);
-    case kBF16: return decode_grid_bf16(p, group, num_seqs, max_context_len, grid);
+    case kF32: return decode_grid_f32(p, group, num_seqs, max_context_len, grid, partition_capacity);
+    case kF16: return decode_grid_f16(p, group, num_seqs, max_context_len, grid, partition_capacity);
+    case kBF16: return decode_grid_bf16(p, group, num_seqs, max_context_len, grid, partition_capacity);
     default: return hipErrorInvalidValue;
   }
 }

@@ -59,16 +59,20 @@ hipError_t launch_copy_blocks(const PoolDesc& p, const int32_t* pairs, int32_t n
 hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 
 // Workgroups of the balanced decode kernel for these sizes (every one
-// resident on the current device at once; PA_DECODE_GRID overrides).
+// resident on the current device at once; PA_DECODE_GRID overrides), and the
+// number of fixed-partition workgroups the device holds at once.
 hipError_t decode_balanced_grid(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
-                                int32_t* grid);
+                                int32_t* grid, int32_t* partition_capacity);
 
 // Per-dtype decode launchers and grid queries (decode_<dtype>.hip).
 hipError_t launch_decode_f32(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
-hipError_t decode_grid_f32(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid);
-hipError_t decode_grid_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid);
-hipError_t decode_grid_bf16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid);
+hipError_t decode_grid_f32(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
+                           int32_t* partition_capacity);
+hipError_t decode_grid_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
+                           int32_t* partition_capacity);
+hipError_t decode_grid_bf16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
+                           int32_t* partition_capacity);
 
 }  // namespace pa

@@ -223,7 +223,8 @@ def test_balanced_split_any_grid(gpu, grid):
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "bf16")
     os.environ["PA_DECODE_GRID"] = str(grid)
     try:
-        got = out_to_f64(run_decode(pk, case, 1, 128, 32, "bf16", out_dtype="f32"))
+        got = out_to_f64(run_decode(pk, case, 1, 128, 32, "bf16", out_dtype="f32",
+                                    partition_tokens=pk.PA_PARTITION_BALANCED))
     finally:
         del os.environ["PA_DECODE_GRID"]
     assert np.all(got[1] == 0.0)
@@ -241,10 +242,11 @@ def test_balanced_workspace_reuse_leaves_counters_zero(gpu):
                    v=to_torch(case["v_pool"], "f16"))
     q, tables, lens = to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(), \
         torch.from_numpy(case["lens"]).cuda()
-    ws = torch.zeros(pk.decode_workspace_bytes(pool, 4, 8, 2500), dtype=torch.uint8, device="cuda")
+    bal = pk.PA_PARTITION_BALANCED
+    ws = torch.zeros(pk.decode_workspace_bytes(pool, 4, 8, 2500, bal), dtype=torch.uint8, device="cuda")
     for n in (4, 2, 4, 4):
         out = pk.decode(pool, q[:n].contiguous(), tables[:n].contiguous(), lens[:n].contiguous(), 2500,
-                        out_dtype="f32", workspace=ws)
+                        out_dtype="f32", workspace=ws, partition_tokens=bal)
         torch.cuda.synchronize()
         assert np.max(np.abs(out_to_f64(out) - want[:n])) <= TOL["f16"]
 
@@ -255,12 +257,31 @@ def test_balanced_rejects_dirty_workspace_under_validation(gpu):
     case = build_case([300, 40], 1, 1, 128, 16, "f16", 8)
     pool = pk.Pool(case["num_blocks"], 16, 1, 128, "f16", k=to_torch(case["k_pool"], "f16"),
                    v=to_torch(case["v_pool"], "f16"))
-    ws = torch.zeros(pk.decode_workspace_bytes(pool, 2, 1, 300), dtype=torch.uint8, device="cuda")
+    bal = pk.PA_PARTITION_BALANCED
+    ws = torch.zeros(pk.decode_workspace_bytes(pool, 2, 1, 300, bal), dtype=torch.uint8, device="cuda")
     ws[-1] = 1                                               # the merge counters sit at the end
     with pytest.raises(pk.PaError) as e:
         pk.decode(pool, to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(),
-                  torch.from_numpy(case["lens"]).cuda(), 300, workspace=ws)
+                  torch.from_numpy(case["lens"]).cuda(), 300, workspace=ws, partition_tokens=bal)
     assert "counters" in str(e.value)
+
+
+@pytest.mark.parametrize("n_seqs", [40, 300])
+def test_whole_sequence_dispatch_order(gpu, n_seqs):
+    """One workgroup per (sequence, kv-head) with a partition longer than any
+    sequence: up to 256 sequences are dispatched longest first (ties by index,
+    here many equal lengths), more in batch order.  Every row must be written
+    exactly by its own sequence's workgroup."""
+    import torch
+    pk = gpu
+    rng = np.random.default_rng(n_seqs)
+    lens = [int(x) for x in rng.choice([0, 1, 17, 64, 200], size=n_seqs)]
+    case = build_case(lens, 2, 2, 64, 16, "f16", n_seqs, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
+    for partition in (208, pk.PA_PARTITION_BALANCED):
+        got = out_to_f64(run_decode(pk, case, 2, 64, 16, "f16", out_dtype="f32", partition_tokens=partition))
+        assert np.max(np.abs(got - want)) <= TOL["f16"], partition
+    assert np.all(got[np.array(lens) == 0] == 0.0)
 
 
 def test_decode_rejects_bad_metadata_under_validation(gpu):
