@@ -249,19 +249,20 @@ def kernel_source_hash():
 
 
 def recorded_traffic(workload):
-    """HBM bytes per decode call from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+    """(HBM bytes per decode call, their ratio to the algorithmic bytes of the
+    counted run) from the committed counter summary, if it was taken on the
+    current kernel source (else (None, None))."""
     path = os.path.join(PROFILES, f"decode_{workload}_traffic.txt")
     if not os.path.exists(path):
-        return None
+        return None, None
     rec = None
     for line in open(path):
         line = line.strip()
         if line.startswith("{"):
             rec = json.loads(line)
     if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_call")
+        return None, None
+    return rec.get("hbm_bytes_per_call"), round(rec["hbm_bytes_per_call"] / rec["algorithmic_bytes_per_call"], 4)
 
 
 def copy_probe(mib):
@@ -334,7 +335,7 @@ def main():
     achieved = per_call_bytes / mean_dec_s / 1e9
     value = total_kv / elapsed / 1e9
     layers = len(st["pools"])
-    traffic = recorded_traffic(w.name)
+    traffic, traffic_ratio = recorded_traffic(w.name)
     dec_sorted = sorted(dec_ms)
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seq-steps/s, 7B shape",
@@ -376,6 +377,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_over_algorithmic": traffic_ratio,
             "algorithmic_bytes_per_call": int(per_call_bytes),
         },
         "cpu_baseline": None,
