@@ -196,14 +196,270 @@ struct Chunk {
 // per batch, and the buffers through which the NW waves merge their results.
 constexpr int kTableBatch = 512;   // block ids staged per batch (a multiple of every CT / BS)
 
-template <int NW, int G, int D>
+// The matrix-core path: 16-bit K/V, blocks of at least 16 tokens (one 16-token
+// MFMA tile never straddles a block) and at least 4 query rows per kv-head
+// (below that the contraction is too thin to beat v_dot2).
+template <int DT, int BS, int G>
+constexpr bool kUseMfma = DT != kF32 && BS >= 16 && G >= 4;
+
+template <int NW, int G, int D, bool MFMA>
 struct WaveMerge {
   float o[NW][G][D];
   float m[NW][G];
   float l[NW][G];
   int bad[NW];
   int32_t tbl[kTableBatch];   // physical block ids, -1 for an id outside the pool
+  // matrix-core path: each wave's V tile, 16 tokens × D, rows padded so the
+  // transposed reads of the four lane quarters fall in distinct banks
+  uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 16 : 1];
 };
+
+// ---------------------------------------------------------------------------
+// Matrix-core inner loop (16-bit K/V, G ≥ 4 query rows per kv-head).
+//
+// Per wave and 16-token chunk:
+//   S  = K·Qᵀ        16 tokens × 16 rows (rows ≥ G are zero), D/32 MFMA
+//                    16x16x32 steps; lane l loads token l%16, dims
+//                    [32i + 8(l/16), +8) of the K tile, which is exactly the
+//                    A operand, and holds S[tokens 4(l/16)..+3][row l%16].
+//   softmax per row  the four lanes of a row (l, l±16, l±32) share the max;
+//                    each keeps a partial sum.
+//   Oᵀ += Vᵀ·Pᵀ      D/16 MFMA 16x16x16 tiles; Pᵀ is the lane's own four
+//                    probabilities (the B operand layout), split into a
+//                    16-bit head and a 16-bit remainder so the product keeps
+//                    ~16 bits of each weight; Vᵀ is read transposed from the
+//                    wave's V tile in LDS.  Lane l then owns
+//                    O[row l%16][dims 16b + 4(l/16)..+3], so the per-row
+//                    rescale by 2^(m_old − m_new) is lane-local.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_k32(const uint4& a, const uint4& b, f32x4_t c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                  0, 0);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_k16(const uint2& a, const uint2& b, f32x4_t c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b), c,
+                                                     0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                                 0, 0);
+  }
+}
+
+// x rounded to the 16-bit type (nearest-even) and back, as bits and value.
+template <int DT>
+__device__ __forceinline__ uint16_t round16(float x, float* back) {
+  if constexpr (DT == kBF16) {
+    const uint16_t h = f32_to_bf16_rne(x);
+    *back = __uint_as_float(static_cast<uint32_t>(h) << 16);
+    return h;
+  } else {
+    const _Float16 h = static_cast<_Float16>(x);
+    *back = static_cast<float>(h);
+    return __builtin_bit_cast(uint16_t, h);
+  }
+}
+
+template <int DT, int D, int BS, int G, int NW, typename Emit>
+__device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+                                                  const char* __restrict__ q, const int32_t* __restrict__ table,
+                                                  int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
+                                                  int32_t t_begin, int32_t t_end, float scale_log2,
+                                                  WaveMerge<NW, G, D, true>& sh, Emit&& emit) {
+  constexpr int EB = 2;
+  constexpr int ROW = D * EB;          // bytes per token row
+  constexpr int CT = 16;               // tokens per chunk (the MFMA M dimension)
+  constexpr int NKL = D / 32;          // 16-byte loads per lane per tensor per chunk
+  constexpr int NB = D / 16;           // output tiles of 16 dims
+  constexpr int64_t TILE = static_cast<int64_t>(BS) * ROW;
+  static_assert(BS % CT == 0 && G <= 16, "matrix-core path needs 16-token tiles and ≤ 16 rows");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tl = lane & 15;   // token (K/V loads, S/P columns) or row (Q, O) of this lane
+  const int qd = lane >> 4;   // quarter: dim slice of the loads, token group of S/P
+  const int q_heads = kv_heads * G;
+
+  // Qᵀ operand: row tl (zero for tl ≥ G), dims [32i + 8qd, +8)
+  const char* q_row = q + ((static_cast<int64_t>(s) * q_heads + g * G + min(tl, G - 1)) * D) * EB + qd * 16;
+  uint4 qop[NKL];
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(q_row + i * 64);
+    qop[i] = tl < G ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float m = kNegBig, l = 0.f;
+  f32x4_t ob[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) ob[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool bad_block = false;
+  const int32_t lane_off = tl * ROW + qd * 16;
+
+  const int32_t blk_first = t_begin / BS;
+  const int32_t blk_last = (t_end - 1) / BS;
+  for (int32_t bb = blk_first; bb <= blk_last; bb += kTableBatch) {
+    const int32_t nb = min(kTableBatch, blk_last - bb + 1);
+    __syncthreads();   // the previous batch's ids are no longer read
+    for (int i = threadIdx.x; i < nb; i += NW * 64) {
+      const int32_t phys = table[bb + i];
+      sh.tbl[i] = static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks) ? phys : -1;
+    }
+    __syncthreads();
+    const int32_t tb = max(t_begin, bb * BS);
+    const int32_t te = min(t_end, (bb + nb) * BS);
+    const int32_t nchunks = (te - tb + CT - 1) / CT;
+
+    // Issue chunk c's K and V loads (live = false: read q instead, which is
+    // valid and cache-resident).  Rows past te inside the block may be read;
+    // they are masked before use.
+    auto load_chunk = [&](int32_t c, bool live, uint4 (&kb)[NKL], uint4 (&vb)[NKL]) {
+      const int32_t tok0 = tb + (live ? c : 0) * CT;
+      int32_t phys = sh.tbl[tok0 / BS - bb];
+      if (phys < 0) {
+        bad_block = true;
+        phys = 0;
+      }
+      const int64_t tile = (static_cast<int64_t>(phys) * kv_heads + g) * TILE + (tok0 % BS) * ROW + lane_off;
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) {
+        kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile + i * 64 : q_row);
+        vb[i] = *reinterpret_cast<const uint4*>(live ? v_pool + tile + i * 64 : q_row);
+      }
+    };
+
+    auto consume_chunk = [&](int32_t c, const uint4 (&kb)[NKL], const uint4 (&vb)[NKL]) {
+      const int32_t tok0 = tb + c * CT;
+      // S = K·Qᵀ
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) sacc = mfma_k32<DT>(kb[i], qop[i], sacc);
+      // this lane's V row into the wave's tile; padding rows become zero
+      // (they may hold NaN, and 0·NaN would poison the product)
+      const bool row_valid = tok0 + tl < te;
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) {
+        *reinterpret_cast<uint4*>(&sh.vt[wave][tl][32 * i + 8 * qd]) =
+            row_valid ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
+      // online softmax of row tl over tokens 4qd..4qd+3
+      float sc[4];
+      bool valid[4];
+      float mx = kNegBig;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        valid[r] = tok0 + 4 * qd + r < te;
+        sc[r] = sacc[r] * scale_log2;
+        if (valid[r]) mx = fmaxf(mx, sc[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m, mx);
+      const float alpha = exp2f_fast(m - m_new);
+      float p[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = valid[r] ? exp2f_fast(sc[r] - m_new) : 0.f;
+        psum += p[r];
+      }
+      l = l * alpha + psum;
+      m = m_new;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ob[b] *= alpha;
+      // Pᵀ operand as 16-bit head + remainder
+      uint16_t ph[4], pl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float back, back2;
+        ph[r] = round16<DT>(p[r], &back);
+        pl[r] = round16<DT>(p[r] - back, &back2);
+      }
+      const uint2 phi = make_uint2(ph[0] | (static_cast<uint32_t>(ph[1]) << 16), ph[2] | (static_cast<uint32_t>(ph[3]) << 16));
+      const uint2 plo = make_uint2(pl[0] | (static_cast<uint32_t>(pl[1]) << 16), pl[2] | (static_cast<uint32_t>(pl[3]) << 16));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the V tile is written …
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");   // … before any lane reads it back
+      // Oᵀ += Vᵀ·Pᵀ: lane reads dim 16b + tl of tokens 4qd..4qd+3
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint32_t v0 = sh.vt[wave][4 * qd + 0][16 * b + tl];
+        const uint32_t v1 = sh.vt[wave][4 * qd + 1][16 * b + tl];
+        const uint32_t v2 = sh.vt[wave][4 * qd + 2][16 * b + tl];
+        const uint32_t v3 = sh.vt[wave][4 * qd + 3][16 * b + tl];
+        const uint2 a = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+        ob[b] = mfma_k16<DT>(a, phi, ob[b]);
+        ob[b] = mfma_k16<DT>(a, plo, ob[b]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // reads done before the next chunk's writes
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    uint4 ka[NKL], va[NKL], kb2[NKL], vb2[NKL];
+    int32_t c = wave;
+    load_chunk(c, c < nchunks, ka, va);
+    for (; c < nchunks; c += 2 * NW) {
+      load_chunk(c + NW, c + NW < nchunks, kb2, vb2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume_chunk(c, ka, va);
+      if (c + NW >= nchunks) break;
+      load_chunk(c + 2 * NW, c + 2 * NW < nchunks, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      consume_chunk(c + NW, kb2, vb2);
+    }
+  }
+
+  // The four quarters of a row hold partial sums over their tokens.
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  // Merge the NW waves through LDS and hand each output to emit.
+  if (tl < G) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.o[wave][tl][16 * b + 4 * qd + r] = ob[b][r];
+    }
+    if (qd == 0) {
+      sh.m[wave][tl] = m;
+      sh.l[wave][tl] = l;
+    }
+  }
+  const bool wave_bad = __any(bad_block);
+  if (lane == 0) sh.bad[wave] = wave_bad ? 1 : 0;
+  __syncthreads();
+  bool bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) bad = bad || sh.bad[w] != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int r = idx / D;
+    const int d = idx - r * D;
+    float mm = kNegBig;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sh.m[w][r]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = exp2f_fast(sh.m[w][r] - mm);
+      L += sh.l[w][r] * a;
+      O += sh.o[w][r][d] * a;
+    }
+    emit(r, d, mm, L, O, bad);
+  }
+  __syncthreads();
+}
 
 // ---------------------------------------------------------------------------
 // attend_range: the G query rows of kv-head g of sequence s over tokens
@@ -229,7 +485,12 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
                                              const char* __restrict__ q, const int32_t* __restrict__ table,
                                              int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
                                              int32_t t_begin, int32_t t_end, float scale_log2,
-                                             WaveMerge<NW, G, D>& sh, Emit&& emit) {
+                                             WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
+  if constexpr (kUseMfma<DT, BS, G>) {
+    attend_range_mfma<DT, D, BS, G, NW>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
+                                        scale_log2, sh, emit);
+    return;
+  } else {
   using S = Shape<DT, D>;
   using CK = Chunk<DT, D, BS>;
   constexpr int ELEMS = S::ELEMS, LPT = S::LPT, TPL = S::TPL, ROW = S::ROW;
@@ -444,6 +705,7 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
     emit(r, d, mm, L, O, bad);
   }
   __syncthreads();
+  }
 }
 
 // Write zero rows (an empty context) or NaN rows (an invalid length) for all
@@ -520,7 +782,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
   const int32_t t_begin = p * part_tokens;
   const int32_t t_end = min(t_begin + part_tokens, len_c);
   const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
-  __shared__ WaveMerge<NW, G, D> sh;
+  __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
   attend_range<DT, D, BS, G, NW>(
       k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
@@ -819,7 +1081,7 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
   int32_t s = static_cast<int32_t>(sh_found[0]);
   int64_t P = sh_found[1];
   __shared__ int sh_last;
-  __shared__ WaveMerge<NW, G, D> sh;
+  __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
   for (; s < num_seqs; ++s) {
     const int32_t len = context_lens[s];
     const int64_t c = seq_chunks<CT>(len, max_ctx);
