@@ -802,18 +802,51 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
 
 // ---------------------------------------------------------------------------
 // decode_reduce_kernel: merge the partitions of sequences longer than one.
-//   grid = (D / 32, q_heads, num_seqs), block = 256 = 32 dims × 8 partition lanes
+//   grid = (q_heads, num_seqs), block = 256 threads; one workgroup per row.
 //   out = Σ_p 2^(m_p − M) o_p / Σ_p 2^(m_p − M) l_p with M = max_p m_p.
+//   The per-partition weights 2^(m_p − M) are computed once into LDS (up to
+//   kReduceLds partitions; beyond that they are recomputed on the fly), then
+//   kReduceThreads/D partition lanes per output element accumulate it with
+//   loads coalesced over d.
 // ---------------------------------------------------------------------------
+constexpr int kReduceThreads = 512;
+constexpr int kReduceLds = 4096;
+
+__device__ __forceinline__ float block_reduce_max(float v, float* sh /*[8]*/) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int w = 1; w < kReduceThreads / 64; ++w) r = fmaxf(r, sh[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_reduce_sum(float v, float* sh /*[8]*/) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < kReduceThreads / 64; ++w) r += sh[w];
+  __syncthreads();
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(void* __restrict__ out, int32_t out_dtype,
-                                                            const float* __restrict__ part_ml,
-                                                            const float* __restrict__ part_o,
-                                                            const int32_t* __restrict__ context_lens,
-                                                            int32_t q_heads, int32_t max_parts,
-                                                            int32_t part_tokens, int32_t max_ctx) {
-  const int s = blockIdx.z;
-  const int h = blockIdx.y;
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __restrict__ out, int32_t out_dtype,
+                                                                       const float* __restrict__ part_ml,
+                                                                       const float* __restrict__ part_o,
+                                                                       const int32_t* __restrict__ context_lens,
+                                                                       int32_t q_heads, int32_t max_parts,
+                                                                       int32_t part_tokens, int32_t max_ctx) {
+  constexpr int LANES = kReduceThreads / D;   // partition lanes per output element
+  const int s = blockIdx.y;
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
@@ -823,42 +856,43 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(void* __restrict__ o
   const float* ml = part_ml + row * max_parts * 2;
   const float* po = part_o + row * max_parts * D;
 
-  __shared__ float sh_red[256];
-  // M = max over partitions
+  __shared__ float sh_red[kReduceThreads / 64];
+  __shared__ float sh_w[kReduceLds];
+  __shared__ float sh_acc[LANES][D];
   float mm = kNegBig;
-  for (int pp = threadIdx.x; pp < nparts; pp += 256) mm = fmaxf(mm, ml[2 * pp]);
-  sh_red[threadIdx.x] = mm;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) sh_red[threadIdx.x] = fmaxf(sh_red[threadIdx.x], sh_red[threadIdx.x + w]);
-    __syncthreads();
+  for (int p = tid; p < nparts; p += kReduceThreads) mm = fmaxf(mm, ml[2 * p]);
+  const float M = block_reduce_max(mm, sh_red);
+  float part = 0.f;
+  for (int p = tid; p < nparts; p += kReduceThreads) {
+    const float wgt = exp2f_fast(ml[2 * p] - M);
+    if (p < kReduceLds) sh_w[p] = wgt;
+    part += ml[2 * p + 1] * wgt;   // a NaN sum marks a partition that met a bad block id
   }
-  mm = sh_red[0];
-  __syncthreads();
-  // L = Σ l_p 2^(m_p - M)
-  float L = 0.f;
-  for (int pp = threadIdx.x; pp < nparts; pp += 256) L += ml[2 * pp + 1] * exp2f_fast(ml[2 * pp] - mm);
-  sh_red[threadIdx.x] = L;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) sh_red[threadIdx.x] += sh_red[threadIdx.x + w];
-    __syncthreads();
+  const float L = block_reduce_sum(part, sh_red);   // its barriers also publish sh_w
+  const int d = tid % D;
+  const int pl = tid / D;
+  // four independent accumulators keep four loads in flight per thread
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int p = pl;
+  for (; p + 3 * LANES < nparts; p += 4 * LANES) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pp = p + k * LANES;
+      const float wgt = pp < kReduceLds ? sh_w[pp] : exp2f_fast(ml[2 * pp] - M);
+      acc[k] = __builtin_fmaf(wgt, po[static_cast<int64_t>(pp) * D + d], acc[k]);
+    }
   }
-  L = sh_red[0];
-  __syncthreads();
-  // O[d] = Σ_p 2^(m_p - M) o_p[d], partitions strided over 8 lanes groups
-  const int dl = threadIdx.x & 31;
-  const int pl = threadIdx.x >> 5;
-  const int d = blockIdx.x * 32 + dl;
-  float acc = 0.f;
-  for (int pp = pl; pp < nparts; pp += 8) acc += po[static_cast<int64_t>(pp) * D + d] * exp2f_fast(ml[2 * pp] - mm);
-  sh_red[threadIdx.x] = acc;
+  for (; p < nparts; p += LANES) {
+    const float wgt = p < kReduceLds ? sh_w[p] : exp2f_fast(ml[2 * p] - M);
+    acc[0] = __builtin_fmaf(wgt, po[static_cast<int64_t>(p) * D + d], acc[0]);
+  }
+  sh_acc[pl][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (pl == 0) {
     float O = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) O += sh_red[k * 32 + dl];
-    const float x = bad_len ? qnan() : (L > 0.f ? O / L : 0.f);
+    for (int k = 0; k < LANES; ++k) O += sh_acc[k][d];
+    const float x = bad_len ? qnan() : (L > 0.f ? O / L : (L != L ? qnan() : 0.f));
     store_out(out, out_dtype, row * D + d, x);
   }
 }
@@ -1226,7 +1260,7 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
                      a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(D / 32, a.q_heads, a.num_seqs), dim3(256), 0, stream, a.out,
+  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.q_heads, a.num_seqs), dim3(kReduceThreads), 0, stream, a.out,
                      a.out_dtype, a.part_ml, a.part_o, a.context_lens, a.q_heads, a.max_parts,
                      a.partition_tokens, a.max_context_len);
   return hipGetLastError();
