@@ -173,6 +173,28 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
 
 
 # ----------------------------------------------------------------------------
+# memory accounting at the end of the run (the pages' utilisation measures)
+# ----------------------------------------------------------------------------
+CONTIGUOUS_MAX_LEN = {"mha7b_fp16": 2048, "gqa70b_bf16": 4096, "prefix_share_fp16": 2048,
+                      "long_splitk_bf16": 131072, "tiny_fp32": 16}
+
+
+def memory_accounting(bm, w):
+    """Slots holding a token ÷ slots reserved, for the paged pool (from the block
+    manager's counters) and for a contiguous reservation of the workload's maximum
+    length per sequence; and logical ÷ physical blocks (sharing)."""
+    st = bm.stats()
+    max_len = CONTIGUOUS_MAX_LEN.get(w.name, 0)
+    paged = st["filled_slots"] / max(1, st["used_blocks"] * st["block_size"])
+    contiguous = st["logical_tokens"] / max(1, st["num_seqs"] * max_len) if max_len else None
+    return {"paged_slot_utilisation": round(paged, 4),
+            "contiguous_slot_utilisation": None if contiguous is None else round(contiguous, 4),
+            "contiguous_max_len": max_len,
+            "logical_over_physical_blocks": round(st["logical_blocks"] / max(1, st["used_blocks"]), 3),
+            "used_blocks": st["used_blocks"], "pool_blocks": st["num_blocks"]}
+
+
+# ----------------------------------------------------------------------------
 # CPU oracle sample
 # ----------------------------------------------------------------------------
 def cpu_baseline(w, sc, budget_s):
@@ -386,6 +408,7 @@ def main():
         },
         "cpu_baseline": None,
     }
+    result["memory"] = memory_accounting(st["bm"], w)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
