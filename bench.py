@@ -126,6 +126,7 @@ def split_meta(flat, B, stride):
 # ----------------------------------------------------------------------------
 def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
     """n_steps decode steps; returns per-step KV bytes read by decode."""
+    import numpy as np
     import torch
     from paged_kv_cache_355_amd._lib import lib, check
 
@@ -133,15 +134,19 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     B, stride = st["B"], st["stride"]
-    ids_ptr = st["ids"].ctypes.data
     row_bytes = 2 * w.kv_heads * w.head_dim * pk.api.ELEM_BYTES[w.dtype]   # K + V per token
     kv_bytes = []
     for i in range(n_steps):
         hb = hbufs[(step0 + i) % len(hbufs)]
         if hb.copied is not None:
             hb.copied.synchronize()
-        n_cow = st["bm"].step_into(ids_ptr, B, hb.slots.data_ptr(), hb.pairs.data_ptr(), hb.tables.data_ptr(),
-                                   stride, hb.lens.data_ptr())
+        # the scheduler arranges the batch for dispatch (long sequences first,
+        # prefix siblings adjacent) before the step's metadata is written
+        order = st["bm"].dispatch_order(st["ids"])
+        if np.any(order != np.arange(B)):
+            st["ids"] = np.ascontiguousarray(st["ids"][order])
+        n_cow = st["bm"].step_into(st["ids"].ctypes.data, B, hb.slots.data_ptr(), hb.pairs.data_ptr(),
+                                   hb.tables.data_ptr(), stride, hb.lens.data_ptr())
         max_len = int(hb.lens_np.max())
         dev["flat"].copy_(hb.flat, non_blocking=True)
         if hb.copied is None:

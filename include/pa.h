@@ -179,9 +179,10 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
  *           the batch has at least as many (sequence, kv-head) units as the
  *           device holds workgroups at once, one workgroup per unit with no
  *           split; else the balanced split.
- *     With fixed partitions and at most 256 sequences, the longest sequences
- *     are dispatched first so the short ones fill the gaps at the end (the
- *     results do not depend on the order).
+ *     With fixed partitions (and in the automatic whole-sequence case)
+ *     workgroups start in batch order, sequence 0 first; arrange the batch
+ *     with pa_bm_dispatch_order to run long sequences first.  Results do not
+ *     depend on the order.
  *   workspace: device memory of ≥ pa_decode_workspace_bytes(...) bytes,
  *     256-byte aligned; may be NULL when that is 0.  The balanced split keeps
  *     merge counters at the end of the workspace_bytes it is given: a new
@@ -277,6 +278,21 @@ pa_status pa_bm_token_slots(const pa_bm* bm, int64_t seq_id, int32_t first, int3
  * them, without appending. */
 pa_status pa_bm_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* block_tables,
                        int32_t stride, int32_t* context_lens);
+
+/* Dispatch order for a decode batch of n sequences: order[k] (host int32[n],
+ * caller-owned) receives the batch position to place k-th.  pa_decode starts
+ * its workgroups in batch order, so a batch arranged this way runs the long
+ * sequences first and lets the short ones fill the tail (longest processing
+ * time first), and keeps sequences that share a prefix side by side so their
+ * common blocks are read at about the same time ([P2] §3.4; [P1]
+ * "跨请求的内存共享").  Sequences whose first block is the same physical
+ * block form a group; groups are ordered by their longest member
+ * (descending), then by their lowest position; members by length
+ * (descending), then by position.  An empty sequence is a group of its own
+ * with length 0.  With no sharing this is a stable sort by length, longest
+ * first.  Duplicate ids are allowed (each position is placed once).
+ * Errors: PA_ERR_INVALID, PA_ERR_NOT_FOUND. */
+pa_status pa_bm_dispatch_order(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* order);
 
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc);
 

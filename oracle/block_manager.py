@@ -39,6 +39,11 @@ implementations agree bit for bit):
    batch needs, nothing changes and ``NoBlocksError`` is raised.
 5. ``free_seq`` decrements refcounts in table order; blocks reaching zero join
    the tail of the free list in that order.
+
+``dispatch_order`` is not from the pages: it is the library's scheduling
+choice for a decode batch (longest processing time first over groups of
+sequences that share their first physical block), stated here so that the
+host implementation can be checked against a plain sort.
 """
 from collections import deque
 
@@ -196,6 +201,24 @@ class OracleBlockManager:
             raise ValueError("token range outside the sequence")
         bs = self.block_size
         return [seq.table[t // bs] * bs + t % bs for t in range(first, first + count)]
+
+    def dispatch_order(self, seq_ids):
+        """Batch positions in dispatch order.  A group is the set of batch
+        sequences whose first block is the same physical block (an empty
+        sequence is alone); groups go longest member first, then by their
+        lowest position; inside a group, longer sequences first, then lower
+        position."""
+        members = {}
+        for pos, s in enumerate(seq_ids):
+            table = self.seqs[s].table
+            group = table[0] if table else ("empty", pos)
+            members.setdefault(group, []).append(pos)
+        keys = []
+        for group, positions in members.items():
+            longest = max(self.seqs[seq_ids[p]].length for p in positions)
+            for p in positions:
+                keys.append((-longest, min(positions), -self.seqs[seq_ids[p]].length, p))
+        return [k[3] for k in sorted(keys)]
 
     def padded_tables(self, seq_ids, stride, pad=-1):
         """Block tables of ``seq_ids`` as rows of ``stride`` entries, padded with ``pad``."""

@@ -59,6 +59,7 @@ SIGNATURES = {
     "pa_bm_block_table": (c_i32, [c_p, c_i64, c_p, c_i32, c_p, c_p]),
     "pa_bm_token_slots": (c_i32, [c_p, c_i64, c_i32, c_i32, c_p]),
     "pa_bm_tables": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_p]),
+    "pa_bm_dispatch_order": (c_i32, [c_p, c_p, c_i32, c_p]),
     "pa_bm_refcount": (c_i32, [c_p, c_i32, c_p]),
     "pa_bm_free_list": (c_i32, [c_p, c_p, c_i32, c_p]),
     "pa_bm_stats": (c_i32, [c_p, c_p]),

@@ -233,6 +233,15 @@ class BlockManager:
                                  lens.ctypes.data), "pa_bm_tables")
         return tables, lens
 
+    def dispatch_order(self, seq_ids):
+        """Batch positions in the order to dispatch them (int32 array): long
+        sequences first, prefix-sharing sequences side by side."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        order = np.empty(max(ids.shape[0], 1), dtype=np.int32)
+        check(lib().pa_bm_dispatch_order(self.handle, ids.ctypes.data, ids.shape[0], order.ctypes.data),
+              "pa_bm_dispatch_order")
+        return order[:ids.shape[0]]
+
     def refcount(self, block):
         rc = ctypes.c_int32()
         check(lib().pa_bm_refcount(self.handle, int(block), ctypes.addressof(rc)), "pa_bm_refcount")

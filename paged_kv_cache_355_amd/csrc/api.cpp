@@ -511,6 +511,12 @@ pa_status pa_bm_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32
   return PA_OK;
 }
 
+pa_status pa_bm_dispatch_order(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* order) {
+  if (!bm || n < 0 || (n > 0 && (!seq_ids || !order))) return fail(PA_ERR_INVALID, "bad arguments");
+  std::string why;
+  return map_bm(bm->impl.dispatch_order(seq_ids, n, order, &why), why);
+}
+
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc) {
   if (!bm || !rc) return fail(PA_ERR_INVALID, "NULL pointer");
   if (block < 0 || block >= bm->impl.num_blocks()) return fail(PA_ERR_INVALID, "block outside the pool");

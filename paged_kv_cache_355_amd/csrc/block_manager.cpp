@@ -165,6 +165,48 @@ BmResult BlockManager::step(const int64_t* ids, int32_t n, int32_t* slots, std::
   return BmResult::ok;
 }
 
+BmResult BlockManager::dispatch_order(const int64_t* ids, int32_t n, int32_t* order, std::string* why) const {
+  struct Key {
+    int32_t group_len, group_pos, len, pos;
+  };
+  struct Group {
+    int32_t len, pos;
+  };
+  std::vector<Key> keys(n);
+  std::vector<int32_t> first(n);
+  std::unordered_map<int32_t, Group> groups;   // first block -> longest member, lowest position
+  groups.reserve(static_cast<size_t>(n) * 2);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = seqs_.find(ids[i]);
+    if (it == seqs_.end()) {
+      *why = "unknown sequence " + std::to_string(ids[i]);
+      return BmResult::not_found;
+    }
+    const Seq& s = it->second;
+    first[i] = s.table.empty() ? -1 : s.table.front();
+    keys[i] = {s.length, i, s.length, i};
+    if (first[i] >= 0) {
+      auto g = groups.emplace(first[i], Group{s.length, i});
+      if (!g.second) g.first->second.len = std::max(g.first->second.len, s.length);
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (first[i] >= 0) {
+      const Group& g = groups[first[i]];
+      keys[i].group_len = g.len;
+      keys[i].group_pos = g.pos;
+    }
+  }
+  std::sort(keys.begin(), keys.end(), [](const Key& a, const Key& b) {
+    if (a.group_len != b.group_len) return a.group_len > b.group_len;
+    if (a.group_pos != b.group_pos) return a.group_pos < b.group_pos;
+    if (a.len != b.len) return a.len > b.len;
+    return a.pos < b.pos;
+  });
+  for (int32_t k = 0; k < n; ++k) order[k] = keys[k].pos;
+  return BmResult::ok;
+}
+
 BmResult BlockManager::free_seq(int64_t id, std::string* why) {
   auto it = seqs_.find(id);
   if (it == seqs_.end()) {

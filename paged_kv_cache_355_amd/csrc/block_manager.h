@@ -39,6 +39,13 @@ class BlockManager {
   // Batched append in batch order, all or nothing.  slots[n]; cow pairs are
   // appended to `pairs` as src, dst.
   BmResult step(const int64_t* ids, int32_t n, int32_t* slots, std::vector<int32_t>* pairs, std::string* why);
+  // Dispatch order for a decode batch: order[k] is the batch position to run
+  // k-th.  Sequences whose first block is the same physical block form a
+  // group; groups go by their longest member (descending), then by their
+  // lowest position; members by length (descending), then position.  Empty
+  // sequences are singleton groups of length 0.  With no sharing this is a
+  // stable sort by length, longest first.
+  BmResult dispatch_order(const int64_t* ids, int32_t n, int32_t* order, std::string* why) const;
   BmResult free_seq(int64_t id, std::string* why);
 
   const std::vector<int32_t>* table(int64_t id, int32_t* length) const;

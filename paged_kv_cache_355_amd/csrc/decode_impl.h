@@ -718,56 +718,27 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
   for (int32_t i = threadIdx.x; i < n; i += blockDim.x) store_out(out, out_dtype, first + i, value);
 }
 
-// Batches of at most this many sequences are dispatched longest first.
-constexpr int kRankMax = 256;
-
-// The sequence whose length ranks `rank` in decreasing order (ties by index;
-// empty and invalid lengths count as 0).  All threads call it; O(num_seqs)
-// LDS reads per thread.
-template <int NW>
-__device__ __forceinline__ int32_t seq_of_rank(int32_t rank, const int32_t* __restrict__ context_lens,
-                                               int32_t num_seqs, int32_t max_ctx) {
-  __shared__ int32_t sh_len[kRankMax];
-  __shared__ int32_t sh_seq;
-  for (int32_t i = threadIdx.x; i < num_seqs; i += NW * 64) {
-    const int32_t len = context_lens[i];
-    sh_len[i] = (len < 0 || len > max_ctx) ? 0 : len;
-  }
-  if (threadIdx.x == 0) sh_seq = rank;   // every rank is taken exactly once; this is only a default
-  __syncthreads();
-  for (int32_t t = threadIdx.x; t < num_seqs; t += NW * 64) {
-    const int32_t lt = sh_len[t];
-    int32_t r = 0;
-    for (int32_t u = 0; u < num_seqs; ++u) {
-      const int32_t lu = sh_len[u];
-      r += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
-    }
-    if (r == rank) sh_seq = t;
-  }
-  __syncthreads();
-  return sh_seq;
-}
-
 // ---------------------------------------------------------------------------
 // decode_partition_kernel (fixed partitions)
 //   grid  = (max_parts, kv_heads, num_seqs), block = NW × 64 threads
 //   Unit (s, g, p) covers tokens [p·P, min((p+1)·P, len_s)) of sequence s,
-//   kv-head g, and the G query heads g·G … g·G+G-1.  With at most kRankMax
-//   sequences, blockIdx.z is a rank: the longest sequences are dispatched
-//   first and the short ones fill the gaps at the end (which workgroup
-//   computes a unit changes nothing in its result).
+//   kv-head g, and the G query heads g·G … g·G+G-1.  Workgroups start in
+//   linear order (x fastest), so the batch order is the dispatch order: the
+//   host scheduler puts long sequences first and prefix-sharing ones side by
+//   side (pa_bm_dispatch_order); which workgroup computes a unit changes
+//   nothing in its result.  Workgroup w runs on XCD w mod 8, so with one
+//   partition and kv_heads a multiple of 8, kv-head g of every sequence lands
+//   on XCD g mod 8 and adjacent siblings find their shared tiles in its L2.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BS, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
-    int32_t num_seqs, int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
-    float scale_log2) {
+    int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2) {
   const int p = blockIdx.x;
   const int g = blockIdx.y;
-  const int s = num_seqs <= kRankMax ? seq_of_rank<NW>(blockIdx.z, context_lens, num_seqs, max_ctx)
-                                     : static_cast<int>(blockIdx.z);
+  const int s = blockIdx.z;
   const int q_heads = kv_heads * G;
 
   const int32_t len = context_lens[s];
@@ -1256,8 +1227,8 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
-                     a.table_stride, a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len,
-                     a.max_parts, a.partition_tokens, a.scale_log2);
+                     a.table_stride, a.context_lens, p.num_blocks, p.kv_heads, a.max_context_len, a.max_parts,
+                     a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.q_heads, a.num_seqs), dim3(kReduceThreads), 0, stream, a.out,

@@ -7,7 +7,9 @@
 //   * every table has ceil(length / block_size) entries;
 //   * the slots of one step are distinct and lie in their sequence's table;
 //   * a copy-on-write pair copies the writer's old last block into a block
-//     that was free, and calls that fail change nothing.
+//     that was free, and calls that fail change nothing;
+//   * a dispatch order is a permutation of the batch positions with groups
+//     (same first block) contiguous and longest members never rising.
 // Exit status 0 means every check held; a sanitizer report aborts.
 #include <algorithm>
 #include <cstdio>
@@ -119,6 +121,32 @@ int main(int argc, char** argv) {
         }
         const BmResult r = bm.step(batch.data(), static_cast<int32_t>(batch.size()), slots.data(), &pairs, &why);
         if (r == BmResult::ok) {
+          std::vector<int32_t> order(batch.size(), -1);
+          CHECK(bm.dispatch_order(batch.data(), static_cast<int32_t>(batch.size()), order.data(), &why) ==
+                BmResult::ok);
+          std::vector<int32_t> sorted_order(order);
+          std::sort(sorted_order.begin(), sorted_order.end());
+          for (size_t i = 0; i < batch.size(); ++i) CHECK(sorted_order[i] == static_cast<int32_t>(i));
+          std::set<int32_t> done_groups;
+          int32_t prev_group = -2, prev_max = 1 << 30;
+          for (size_t k = 0; k < order.size(); ++k) {
+            int32_t len = 0;
+            const std::vector<int32_t>* t = bm.table(batch[order[k]], &len);
+            const int32_t group = t->empty() ? -1 - order[k] : t->front();
+            if (group != prev_group) {
+              CHECK(done_groups.insert(group).second);   // a group appears in one run
+              int32_t longest = 0;
+              for (int64_t id : batch) {
+                int32_t l2 = 0;
+                const std::vector<int32_t>* t2 = bm.table(id, &l2);
+                if (!t2->empty() && !t->empty() && t2->front() == group) longest = std::max(longest, l2);
+              }
+              if (t->empty()) longest = len;
+              CHECK(longest <= prev_max);
+              prev_max = longest;
+              prev_group = group;
+            }
+          }
           std::set<int32_t> seen;
           for (size_t i = 0; i < batch.size(); ++i) {
             CHECK(seen.insert(slots[i]).second);

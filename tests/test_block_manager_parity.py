@@ -55,6 +55,7 @@ def test_workload_scripts_agree(name):
     assert tables.tolist() == ora.padded_tables(sc.measured, stride)
     assert lens.tolist() == [ora.length(s) for s in sc.measured]
     assert lens.tolist() == [sc.lengths_before[s] + 1 for s in sc.measured]
+    assert lib_bm.dispatch_order(sc.measured).tolist() == ora.dispatch_order(sc.measured)
     assert_same_state(lib_bm, ora)
 
 
@@ -144,6 +145,7 @@ class ParityMachine(RuleBasedStateMachine):
         assert slots.tolist() == o_slots
         assert [tuple(p) for p in pairs.tolist()] == o_pairs
         assert lens.tolist() == [self.ora.length(s) for s in ids]
+        assert self.lib.dispatch_order(ids).tolist() == self.ora.dispatch_order(ids)
 
     @precondition(lambda self: self.ora.seqs)
     @rule(data=st.data())

@@ -267,20 +267,25 @@ def test_balanced_rejects_dirty_workspace_under_validation(gpu):
 
 
 @pytest.mark.parametrize("n_seqs", [40, 300])
-def test_whole_sequence_dispatch_order(gpu, n_seqs):
+def test_whole_sequence_batch_order(gpu, n_seqs):
     """One workgroup per (sequence, kv-head) with a partition longer than any
-    sequence: up to 256 sequences are dispatched longest first (ties by index,
-    here many equal lengths), more in batch order.  Every row must be written
-    exactly by its own sequence's workgroup."""
-    import torch
+    sequence; workgroups start in batch order.  Every row matches the oracle,
+    and reversing the batch reverses the rows bit for bit (a unit's result
+    does not depend on when or where it runs).  Many equal lengths."""
     pk = gpu
     rng = np.random.default_rng(n_seqs)
     lens = [int(x) for x in rng.choice([0, 1, 17, 64, 200], size=n_seqs)]
     case = build_case(lens, 2, 2, 64, 16, "f16", n_seqs, scale=1.0)
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
+    rev = dict(case, q=case["q"][::-1].copy(), tables=case["tables"][::-1].copy(), lens=case["lens"][::-1].copy())
     for partition in (208, pk.PA_PARTITION_BALANCED):
         got = out_to_f64(run_decode(pk, case, 2, 64, 16, "f16", out_dtype="f32", partition_tokens=partition))
         assert np.max(np.abs(got - want)) <= TOL["f16"], partition
+        got_rev = out_to_f64(run_decode(pk, rev, 2, 64, 16, "f16", out_dtype="f32", partition_tokens=partition))
+        if partition == 208:
+            assert np.array_equal(got_rev, got[::-1])
+        else:
+            assert np.max(np.abs(got_rev[::-1] - want)) <= TOL["f16"]
     assert np.all(got[np.array(lens) == 0] == 0.0)
 
 

@@ -7,12 +7,16 @@
   expected tables/slots are written out by hand below.
 * A hypothesis state machine checks the invariants the pages imply for any
   call sequence.
+* dispatch_order (a scheduling choice, not the pages') is pinned by a
+  hand-ordered batch, by its reduction to a plain stable sort when nothing is
+  shared, and by the properties any such order must have.
 """
 import json
 import os
 
+import numpy as np
 import pytest
-from hypothesis import settings, strategies as st
+from hypothesis import given, settings, strategies as st
 from hypothesis.stateful import RuleBasedStateMachine, rule, invariant, precondition
 
 from oracle.block_manager import OracleBlockManager, NoBlocksError
@@ -267,3 +271,72 @@ class BMStateMachine(RuleBasedStateMachine):
 
 TestBMStateMachine = BMStateMachine.TestCase
 TestBMStateMachine.settings = settings(max_examples=150, stateful_step_count=40, deadline=None)
+
+
+def test_dispatch_order_hand_example():
+    """Parent P (32 tokens, 2 blocks of 16) forked into C1 and C2, which then
+    grow to 37 and 34 tokens; D has 50 tokens of its own; E is empty.  Batch
+    [E, C2, D, P, C1]: D's group is longest (50) and goes first, then the P
+    group by length (C1 37, C2 34, P 32), then E.  A second batch ties two
+    groups at length 32 (F, 32 tokens of its own): the group seen first in the
+    batch goes first."""
+    bm = OracleBlockManager(32, 16)
+    bm.add_seq("P", 32)
+    bm.fork("P", "C1")
+    bm.fork("P", "C2")
+    for _ in range(5):
+        bm.append_slot("C1")
+    for _ in range(2):
+        bm.append_slot("C2")
+    bm.add_seq("D", 50)
+    bm.add_seq("E", 0)
+    assert bm.dispatch_order(["E", "C2", "D", "P", "C1"]) == [2, 4, 1, 3, 0]
+    bm.add_seq("F", 32)
+    assert bm.dispatch_order(["F", "P", "E"]) == [0, 1, 2]
+    assert bm.dispatch_order(["P", "F", "E"]) == [0, 1, 2]
+    assert bm.dispatch_order(["E", "F", "C2", "P"]) == [2, 3, 1, 0]
+
+
+def test_dispatch_order_without_sharing_is_a_stable_length_sort():
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.choice([0, 1, 5, 16, 17, 40], size=60)]
+    bm = OracleBlockManager(600, 4)
+    for i, n in enumerate(lens):
+        bm.add_seq(i, n)
+    batch = [int(x) for x in rng.permutation(60)]
+    want = sorted(range(60), key=lambda p: -lens[batch[p]])     # Python's sort is stable
+    assert bm.dispatch_order(batch) == want
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 40), st.integers(0, 3), st.integers(0, 9)), min_size=1, max_size=24))
+def test_dispatch_order_properties(spec):
+    """Each spec entry adds a root of n tokens with k forks, each fork grown by
+    g tokens.  Any batch order: a permutation; a group (same first block) is
+    contiguous; group maxima never rise; lengths never rise inside a group."""
+    bm = OracleBlockManager(4096, 4)
+    ids = []
+    for r, (n, k, g) in enumerate(spec):
+        bm.add_seq((r, 0), n)
+        ids.append((r, 0))
+        for c in range(1, k + 1):
+            bm.fork((r, 0), (r, c))
+            for _ in range(g * c % 7):
+                bm.append_slot((r, c))
+            ids.append((r, c))
+    order = bm.dispatch_order(ids)
+    assert sorted(order) == list(range(len(ids)))
+    seq = [ids[p] for p in order]
+    first = [bm.block_table(s)[0][0] if bm.block_table(s)[0] else ("empty", s) for s in seq]
+    length = [bm.length(s) for s in seq]
+    runs = []
+    for f, n in zip(first, length):
+        if runs and runs[-1][0] == f:
+            runs[-1][1].append(n)
+        else:
+            runs.append((f, [n]))
+    assert len({r[0] for r in runs}) == len(runs)                # contiguous groups
+    maxima = [max(r[1]) for r in runs]
+    assert maxima == sorted(maxima, reverse=True)
+    for _, ns in runs:
+        assert ns == sorted(ns, reverse=True)
