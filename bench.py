@@ -26,6 +26,7 @@ workload on this host.
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -277,8 +278,15 @@ def cpu_baseline(w, sc, budget_s):
 # HBM traffic recorded from rocprofv3 counters for this kernel source
 # ----------------------------------------------------------------------------
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the decode kernels' code with // comments and blank
+    space removed, so an edit of comments alone keeps recorded counters valid."""
+    code = []
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        for line in f:
+            line = re.sub(r"//.*$", "", line).strip()
+            if line:
+                code.append(re.sub(r"\s+", " ", line))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def recorded_traffic(workload):

@@ -14,26 +14,31 @@
 //   * The G = q_heads/kv_heads query rows of one kv-head are processed
 //     together and stay in registers, so K and V are read from HBM once per
 //     kv-head.
-//   * A token row (head_dim elements) is spread over LPT lanes with 16 bytes
-//     per lane, so one wave-wide global_load_dwordx4 moves 1 KiB: TPL = 64/LPT
-//     consecutive tokens of one contiguous (block, kv-head) tile.
-//   * Each LPT-lane group keeps its own running max/sum/output for the tokens
-//     it loads, so the hot loop needs no cross-group traffic: scores are
-//     reduced inside the group with DPP row rotations fused into v_add
+//   * Vector path (fp32, or G < 4, or blocks under 16 tokens): a token row
+//     (head_dim elements) is spread over LPT lanes with 16 bytes per lane, so
+//     one wave-wide global_load_dwordx4 moves 1 KiB: TPL = 64/LPT consecutive
+//     tokens of one contiguous (block, kv-head) tile.  Each LPT-lane group
+//     keeps its own running max/sum/output for the tokens it loads; scores
+//     are reduced inside the group with DPP row rotations fused into v_add
 //     (v_dot2 for fp16/bf16 products); groups and waves are merged once per
 //     piece of work at the end.
+//   * Matrix-core path (16-bit K/V, G ≥ 4, blocks of ≥ 16 tokens): 16-token
+//     tiles go through MFMA, S = K·Qᵀ and Oᵀ += Vᵀ·Pᵀ (attend_range_mfma).
 //   * Loads of the next chunk are issued before the current chunk is consumed
 //     (two register buffers).
 //   * Softmax runs in base 2: scores carry scale·log2(e) and v_exp_f32 does 2^x.
 //
-// Two ways of dealing out the work (both exact up to fp32 rounding order):
-//   * Balanced (the default): the (sequence, kv-head) units are laid end to
-//     end on one axis of CT-token chunks and every workgroup of a single,
-//     fully resident grid takes an equal slice of that axis.  Units cut by a
-//     slice boundary produce partial (max, sum, output) records that the last
-//     arriving piece merges, through a fan-in-16 tree for long units, so no
-//     second kernel runs and every CU finishes at the same time whatever the
-//     length mix.
+// Three ways of dealing out the work (all exact up to fp32 rounding order):
+//   * Whole sequences: one workgroup per (sequence, kv-head), started in
+//     batch order; the automatic choice when the batch has at least as many
+//     units as the device holds workgroups at once.
+//   * Balanced (the automatic choice for smaller batches): the (sequence,
+//     kv-head) units are laid end to end on one axis of CT-token chunks and
+//     every workgroup of a single, fully resident grid takes an equal slice
+//     of that axis.  Units cut by a slice boundary produce partial (max, sum,
+//     output) records that the last arriving piece merges, through a
+//     fan-in-16 tree for long units, so no second kernel runs and every CU
+//     finishes at the same time whatever the length mix.
 //   * Fixed partitions (an explicit partition length): one workgroup per
 //     (sequence, kv-head, partition of P tokens) and a second kernel,
 //     decode_reduce_kernel, merges the partitions of longer sequences.
@@ -773,7 +778,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
 
 // ---------------------------------------------------------------------------
 // decode_reduce_kernel: merge the partitions of sequences longer than one.
-//   grid = (q_heads, num_seqs), block = 256 threads; one workgroup per row.
+//   grid = (q_heads, num_seqs), block = kReduceThreads; one workgroup per row.
 //   out = Σ_p 2^(m_p − M) o_p / Σ_p 2^(m_p − M) l_p with M = max_p m_p.
 //   The per-partition weights 2^(m_p − M) are computed once into LDS (up to
 //   kReduceLds partitions; beyond that they are recomputed on the fly), then
