@@ -207,6 +207,14 @@ constexpr int kTableBatch = 512;   // block ids staged per batch (a multiple of 
 template <int DT, int BS, int G>
 constexpr bool kUseMfma = DT != kF32 && BS >= 16 && G >= 4;
 
+// Waves per SIMD the decode kernels are compiled for, where that costs no
+// spills: four (≤ 128 VGPRs) for the vector loop with one or two query rows
+// (the balanced kernel, whose merge code also needs registers, with one);
+// three (≤ 168) for the matrix-core loop of the partition kernel, whose MFMA
+// accumulators then stay in VGPRs; otherwise what the register file allows.
+template <int DT, int BS, int G, bool BALANCED>
+constexpr int kMinWavesPerEU = kUseMfma<DT, BS, G> ? (BALANCED ? 1 : 3) : (G <= (BALANCED ? 1 : 2) ? 4 : 1);
+
 template <int NW, int G, int D, bool MFMA>
 struct WaveMerge {
   float o[NW][G][D];
@@ -214,9 +222,11 @@ struct WaveMerge {
   float l[NW][G];
   int bad[NW];
   int32_t tbl[kTableBatch];   // physical block ids, -1 for an id outside the pool
-  // matrix-core path: each wave's V tile, 16 tokens × D, rows padded so the
-  // transposed reads of the four lane quarters fall in distinct banks
-  uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 16 : 1];
+  // matrix-core path: each wave's V tile, 16 tokens × D.  Lane quarter qd
+  // reads rows 4qd..4qd+3; a row of D/2 + 2 dwords puts the quarters 8 banks
+  // apart (4·(D/2 + 2) ≡ 8 mod 32), so one transposed read touches 32
+  // distinct banks.
+  uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
 };
 
 // ---------------------------------------------------------------------------
@@ -277,6 +287,35 @@ __device__ __forceinline__ uint16_t round16(float x, float* back) {
     *back = static_cast<float>(h);
     return __builtin_bit_cast(uint16_t, h);
   }
+}
+
+// A 16-byte K/V load.  STREAM selects the non-temporal (streaming) cache
+// policy, for tiles that no other workgroup of the call reads: it keeps them
+// from displacing other lines and measured faster on the vector path.  Tiles
+// shared by several sequences of the batch take the default policy, so the
+// siblings that read them next find them in L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_kv(const char* p) {
+  if constexpr (STREAM) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
+// Whether sequence s shares its first physical block with a batch neighbour
+// (s − 1 or s + 1), i.e. reads a prefix that a sibling scheduled next to it
+// also reads.  Rows of empty sequences may hold anything; a false match only
+// selects the default cache policy.
+__device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ block_tables, int32_t table_stride,
+                                                   int32_t s, int32_t num_seqs) {
+  const int32_t first = block_tables[static_cast<int64_t>(s) * table_stride];
+  bool shared = false;
+  if (s > 0) shared = shared || block_tables[static_cast<int64_t>(s - 1) * table_stride] == first;
+  if (s + 1 < num_seqs) shared = shared || block_tables[static_cast<int64_t>(s + 1) * table_stride] == first;
+  return shared;
 }
 
 template <int DT, int D, int BS, int G, int NW, typename Emit>
@@ -357,8 +396,10 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       const bool row_valid = tok0 + tl < te;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        *reinterpret_cast<uint4*>(&sh.vt[wave][tl][32 * i + 8 * qd]) =
-            row_valid ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 v = row_valid ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
+        uint2* dst = reinterpret_cast<uint2*>(&sh.vt[wave][tl][32 * i + 8 * qd]);   // rows are 8-byte aligned
+        dst[0] = make_uint2(v.x, v.y);
+        dst[1] = make_uint2(v.z, v.w);
       }
       // online softmax of row tl over tokens 4qd..4qd+3
       float sc[4];
@@ -485,7 +526,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 // Block ids come from LDS, staged kTableBatch at a time, so no global load of
 // the table sits between two chunks.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int BS, int G, int NW, typename Emit>
+template <int DT, int D, int BS, int G, int NW, bool STREAM, typename Emit>
 __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
                                              const char* __restrict__ q, const int32_t* __restrict__ table,
                                              int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
@@ -564,8 +605,8 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
           const int64_t tile = tile_of(tok0) + lane_off;
 #pragma unroll
           for (int i = 0; i < NLC; ++i) {
-            kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile + i * TPL * ROW : q_lane);
-            vb[i] = *reinterpret_cast<const uint4*>(live ? v_pool + tile + i * TPL * ROW : q_lane);
+            kb[i] = load_kv<STREAM>(live ? k_pool + tile + i * TPL * ROW : q_lane);
+            vb[i] = load_kv<STREAM>(live ? v_pool + tile + i * TPL * ROW : q_lane);
           }
         } else {
 #pragma unroll
@@ -574,16 +615,16 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
             // group (always inside an allocated block); its lanes are masked
             const int32_t t = tok0 + i * TPL < te ? tok0 + i * TPL : tok0;
             const int64_t tile = tile_of(t) + lane_off;
-            kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile : q_lane);
-            vb[i] = *reinterpret_cast<const uint4*>(live ? v_pool + tile : q_lane);
+            kb[i] = load_kv<STREAM>(live ? k_pool + tile : q_lane);
+            vb[i] = load_kv<STREAM>(live ? v_pool + tile : q_lane);
           }
         }
       } else {
         int32_t t = tok0 + grp;
         if (t >= te) t = te - 1;
         const int64_t off = tile_of(t) + sub * 16;
-        kb[0] = *reinterpret_cast<const uint4*>(live ? k_pool + off : q_lane);
-        vb[0] = *reinterpret_cast<const uint4*>(live ? v_pool + off : q_lane);
+        kb[0] = load_kv<STREAM>(live ? k_pool + off : q_lane);
+        vb[0] = load_kv<STREAM>(live ? v_pool + off : q_lane);
       }
     };
 
@@ -723,6 +764,26 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
   for (int32_t i = threadIdx.x; i < n; i += blockDim.x) store_out(out, out_dtype, first + i, value);
 }
 
+// attend_range with the cache policy chosen at run time (wave-uniform): the
+// streaming policy unless the tiles are shared with a neighbouring sequence.
+// The matrix-core loop always takes the default policy (streaming loads
+// measured slower there).
+template <int DT, int D, int BS, int G, int NW, typename Emit>
+__device__ __forceinline__ void attend_range_policy(bool shared, const char* __restrict__ k_pool,
+                                                    const char* __restrict__ v_pool, const char* __restrict__ q,
+                                                    const int32_t* __restrict__ table, int32_t s, int32_t g,
+                                                    int32_t kv_heads, int32_t num_blocks, int32_t t_begin,
+                                                    int32_t t_end, float scale_log2,
+                                                    WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
+  if (kUseMfma<DT, BS, G> || shared) {
+    attend_range<DT, D, BS, G, NW, false>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
+                                          scale_log2, sh, emit);
+  } else {
+    attend_range<DT, D, BS, G, NW, true>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
+                                         scale_log2, sh, emit);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // decode_partition_kernel (fixed partitions)
 //   grid  = (max_parts, kv_heads, num_seqs), block = NW × 64 threads
@@ -736,11 +797,12 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
 //   on XCD g mod 8 and adjacent siblings find their shared tiles in its L2.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
+__global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void decode_partition_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
-    int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2) {
+    int32_t num_seqs, int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
+    float scale_log2) {
   const int p = blockIdx.x;
   const int g = blockIdx.y;
   const int s = blockIdx.z;
@@ -759,8 +821,9 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
   const int32_t t_end = min(t_begin + part_tokens, len_c);
   const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
   __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
-  attend_range<DT, D, BS, G, NW>(
-      k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
+  attend_range_policy<DT, D, BS, G, NW>(
+      shares_first_block(block_tables, table_stride, s, num_seqs), k_pool, v_pool, q, table, s, g, kv_heads,
+      num_blocks, t_begin, t_end, scale_log2, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
         if (nparts == 1) {
@@ -1002,7 +1065,7 @@ __device__ __forceinline__ void merge_records(float* __restrict__ rec_ml, float*
 //   and resets the counter to zero for the next call.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
+__global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void decode_balanced_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, int32_t* __restrict__ ctr, float* __restrict__ rec_ml,
     float* __restrict__ rec_o, const int32_t* __restrict__ block_tables, int32_t table_stride,
@@ -1100,6 +1163,7 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
     P += c;
     if (c == 0) continue;
     const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
+    const bool shared = shares_first_block(block_tables, table_stride, s, num_seqs);
     for (int32_t g = start > base ? static_cast<int32_t>((start - base) / c) : 0; g < kv_heads; ++g) {
       const int64_t off = base + g * c;
       if (off >= end) break;
@@ -1108,8 +1172,8 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
       const int32_t t0 = static_cast<int32_t>(a * CT);
       const int32_t t1 = static_cast<int32_t>(min(b * CT, static_cast<int64_t>(len)));
       if (a == 0 && b == c) {   // the whole unit: write the output directly
-        attend_range<DT, D, BS, G, NW>(
-            k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
+        attend_range_policy<DT, D, BS, G, NW>(
+            shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
             [&](int r, int d, float M, float L, float O, bool bad) {
               const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
               store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
@@ -1122,8 +1186,8 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(
       int32_t n = static_cast<int32_t>(slice_owner(off + c - 1, C, W) - first_w + 1);   // pieces
       int32_t idx = static_cast<int32_t>(w - first_w);
       const int64_t my_slot = slot0 + idx;
-      attend_range<DT, D, BS, G, NW>(
-          k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
+      attend_range_policy<DT, D, BS, G, NW>(
+          shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
           [&](int r, int d, float M, float L, float O, bool bad) {
             const int64_t rr = my_slot * G + r;
             st_rec(rec_o + rr * D + d, O);
@@ -1232,8 +1296,8 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
-                     a.table_stride, a.context_lens, p.num_blocks, p.kv_heads, a.max_context_len, a.max_parts,
-                     a.partition_tokens, a.scale_log2);
+                     a.table_stride, a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len,
+                     a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.q_heads, a.num_seqs), dim3(kReduceThreads), 0, stream, a.out,
