@@ -229,6 +229,22 @@ struct WaveMerge {
   uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
 };
 
+// A 16-byte K/V load.  STREAM selects the non-temporal (streaming) cache
+// policy, for tiles that no other workgroup of the call reads: it keeps them
+// from displacing other lines and measured faster on the vector path.  Tiles
+// shared by several sequences of the batch take the default policy, so the
+// siblings that read them next find them in L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_kv(const char* p) {
+  if constexpr (STREAM) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core inner loop (16-bit K/V, G ≥ 4 query rows per kv-head).
 //
@@ -246,6 +262,12 @@ struct WaveMerge {
 //                    wave's V tile in LDS.  Lane l then owns
 //                    O[row l%16][dims 16b + 4(l/16)..+3], so the per-row
 //                    rescale by 2^(m_old − m_new) is lane-local.
+//   Loads            each K load instruction covers 64 bytes of 16 token rows
+//                    (the A layout); the other half of each 128-byte line
+//                    comes with the next instruction, from L2, so K keeps the
+//                    default cache policy.  V only passes through LDS, so it
+//                    is loaded in whole rows (1 KiB contiguous per wave
+//                    instruction) and may stream.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -289,22 +311,6 @@ __device__ __forceinline__ uint16_t round16(float x, float* back) {
   }
 }
 
-// A 16-byte K/V load.  STREAM selects the non-temporal (streaming) cache
-// policy, for tiles that no other workgroup of the call reads: it keeps them
-// from displacing other lines and measured faster on the vector path.  Tiles
-// shared by several sequences of the batch take the default policy, so the
-// siblings that read them next find them in L2.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <bool STREAM>
-__device__ __forceinline__ uint4 load_kv(const char* p) {
-  if constexpr (STREAM) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-}
-
 // Whether sequence s shares its first physical block with a batch neighbour
 // (s − 1 or s + 1), i.e. reads a prefix that a sibling scheduled next to it
 // also reads.  Rows of empty sequences may hold anything; a false match only
@@ -318,7 +324,7 @@ __device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ b
   return shared;
 }
 
-template <int DT, int D, int BS, int G, int NW, typename Emit>
+template <int DT, int D, int BS, int G, int NW, bool STREAM, typename Emit>
 __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
                                                   const char* __restrict__ q, const int32_t* __restrict__ table,
                                                   int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
@@ -330,7 +336,10 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   constexpr int NKL = D / 32;          // 16-byte loads per lane per tensor per chunk
   constexpr int NB = D / 16;           // output tiles of 16 dims
   constexpr int64_t TILE = static_cast<int64_t>(BS) * ROW;
+  constexpr int LPR = ROW / 16;        // lanes per V row in a contiguous load
+  constexpr int RPI = 64 / LPR;        // V rows per load instruction
   static_assert(BS % CT == 0 && G <= 16, "matrix-core path needs 16-token tiles and ≤ 16 rows");
+  static_assert(RPI * NKL == CT, "NKL contiguous loads cover the 16-row V tile");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -351,7 +360,9 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 #pragma unroll
   for (int b = 0; b < NB; ++b) ob[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad_block = false;
-  const int32_t lane_off = tl * ROW + qd * 16;
+  const int32_t lane_off = tl * ROW + qd * 16;                      // K: A-operand layout
+  const int32_t vrow = lane / LPR;                                  // V: row within a load
+  const int32_t v_off = vrow * ROW + (lane % LPR) * 16;
 
   const int32_t blk_first = t_begin / BS;
   const int32_t blk_last = (t_end - 1) / BS;
@@ -377,11 +388,11 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
         bad_block = true;
         phys = 0;
       }
-      const int64_t tile = (static_cast<int64_t>(phys) * kv_heads + g) * TILE + (tok0 % BS) * ROW + lane_off;
+      const int64_t tile = (static_cast<int64_t>(phys) * kv_heads + g) * TILE + (tok0 % BS) * ROW;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile + i * 64 : q_row);
-        vb[i] = *reinterpret_cast<const uint4*>(live ? v_pool + tile + i * 64 : q_row);
+        kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile + lane_off + i * 64 : q_row);
+        vb[i] = load_kv<STREAM>(live ? v_pool + tile + v_off + i * RPI * ROW : q_row);
       }
     };
 
@@ -391,13 +402,13 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NKL; ++i) sacc = mfma_k32<DT>(kb[i], qop[i], sacc);
-      // this lane's V row into the wave's tile; padding rows become zero
+      // this lane's V pieces into the wave's tile; padding rows become zero
       // (they may hold NaN, and 0·NaN would poison the product)
-      const bool row_valid = tok0 + tl < te;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        const uint4 v = row_valid ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
-        uint2* dst = reinterpret_cast<uint2*>(&sh.vt[wave][tl][32 * i + 8 * qd]);   // rows are 8-byte aligned
+        const int row = i * RPI + vrow;
+        const uint4 v = tok0 + row < te ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
+        uint2* dst = reinterpret_cast<uint2*>(&sh.vt[wave][row][(lane % LPR) * 8]);   // rows are 8-byte aligned
         dst[0] = make_uint2(v.x, v.y);
         dst[1] = make_uint2(v.z, v.w);
       }
@@ -533,8 +544,8 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
                                              int32_t t_begin, int32_t t_end, float scale_log2,
                                              WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
   if constexpr (kUseMfma<DT, BS, G>) {
-    attend_range_mfma<DT, D, BS, G, NW>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
-                                        scale_log2, sh, emit);
+    attend_range_mfma<DT, D, BS, G, NW, STREAM>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin,
+                                                t_end, scale_log2, sh, emit);
     return;
   } else {
   using S = Shape<DT, D>;
@@ -766,8 +777,7 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
 
 // attend_range with the cache policy chosen at run time (wave-uniform): the
 // streaming policy unless the tiles are shared with a neighbouring sequence.
-// The matrix-core loop always takes the default policy (streaming loads
-// measured slower there).
+// (The matrix-core loop streams V only; its K loads keep the default policy.)
 template <int DT, int D, int BS, int G, int NW, typename Emit>
 __device__ __forceinline__ void attend_range_policy(bool shared, const char* __restrict__ k_pool,
                                                     const char* __restrict__ v_pool, const char* __restrict__ q,
@@ -775,7 +785,7 @@ __device__ __forceinline__ void attend_range_policy(bool shared, const char* __r
                                                     int32_t kv_heads, int32_t num_blocks, int32_t t_begin,
                                                     int32_t t_end, float scale_log2,
                                                     WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
-  if (kUseMfma<DT, BS, G> || shared) {
+  if (shared) {
     attend_range<DT, D, BS, G, NW, false>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
                                           scale_log2, sh, emit);
   } else {
