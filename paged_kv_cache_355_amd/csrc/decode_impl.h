@@ -227,6 +227,7 @@ struct WaveMerge {
   // apart (4·(D/2 + 2) ≡ 8 mod 32), so one transposed read touches 32
   // distinct banks.
   uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
+  uint16_t kt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];   // K tile, read back in the A layout
 };
 
 // A 16-byte K/V load.  STREAM selects the non-temporal (streaming) cache
@@ -262,12 +263,12 @@ __device__ __forceinline__ uint4 load_kv(const char* p) {
 //                    wave's V tile in LDS.  Lane l then owns
 //                    O[row l%16][dims 16b + 4(l/16)..+3], so the per-row
 //                    rescale by 2^(m_old − m_new) is lane-local.
-//   Loads            each K load instruction covers 64 bytes of 16 token rows
-//                    (the A layout); the other half of each 128-byte line
-//                    comes with the next instruction, from L2, so K keeps the
-//                    default cache policy.  V only passes through LDS, so it
-//                    is loaded in whole rows (1 KiB contiguous per wave
-//                    instruction) and may stream.
+//   Loads            K and V are loaded in whole token rows (1 KiB
+//                    contiguous per wave instruction, so they may stream) and
+//                    pass through the wave's LDS tiles: K is read back in the
+//                    A layout (lane l: token l%16, dims 32i + 8(l/16)..+7),
+//                    V transposed.  Loading K straight into the A layout
+//                    would split every 128-byte line over two instructions.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -360,8 +361,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 #pragma unroll
   for (int b = 0; b < NB; ++b) ob[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad_block = false;
-  const int32_t lane_off = tl * ROW + qd * 16;                      // K: A-operand layout
-  const int32_t vrow = lane / LPR;                                  // V: row within a load
+  const int32_t vrow = lane / LPR;                                  // K/V: row within a load
   const int32_t v_off = vrow * ROW + (lane % LPR) * 16;
 
   const int32_t blk_first = t_begin / BS;
@@ -391,17 +391,34 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       const int64_t tile = (static_cast<int64_t>(phys) * kv_heads + g) * TILE + (tok0 % BS) * ROW;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        kb[i] = *reinterpret_cast<const uint4*>(live ? k_pool + tile + lane_off + i * 64 : q_row);
+        kb[i] = load_kv<STREAM>(live ? k_pool + tile + v_off + i * RPI * ROW : q_row);
         vb[i] = load_kv<STREAM>(live ? v_pool + tile + v_off + i * RPI * ROW : q_row);
       }
     };
 
     auto consume_chunk = [&](int32_t c, const uint4 (&kb)[NKL], const uint4 (&vb)[NKL]) {
       const int32_t tok0 = tb + c * CT;
+      // K rows into the wave's K tile, then read back in the A layout
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) {
+        const int row = i * RPI + vrow;
+        uint2* dst = reinterpret_cast<uint2*>(&sh.kt[wave][row][(lane % LPR) * 8]);
+        dst[0] = make_uint2(kb[i].x, kb[i].y);
+        dst[1] = make_uint2(kb[i].z, kb[i].w);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint4 ka_op[NKL];
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) {
+        const uint2* src = reinterpret_cast<const uint2*>(&sh.kt[wave][tl][32 * i + 8 * qd]);
+        const uint2 lo = src[0], hi = src[1];
+        ka_op[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
       // S = K·Qᵀ
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) sacc = mfma_k32<DT>(kb[i], qop[i], sacc);
+      for (int i = 0; i < NKL; ++i) sacc = mfma_k32<DT>(ka_op[i], qop[i], sacc);
       // this lane's V pieces into the wave's tile; padding rows become zero
       // (they may hold NaN, and 0·NaN would poison the product)
 #pragma unroll
@@ -777,7 +794,6 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
 
 // attend_range with the cache policy chosen at run time (wave-uniform): the
 // streaming policy unless the tiles are shared with a neighbouring sequence.
-// (The matrix-core loop streams V only; its K loads keep the default policy.)
 template <int DT, int D, int BS, int G, int NW, typename Emit>
 __device__ __forceinline__ void attend_range_policy(bool shared, const char* __restrict__ k_pool,
                                                     const char* __restrict__ v_pool, const char* __restrict__ q,
@@ -851,15 +867,19 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
 
 // ---------------------------------------------------------------------------
 // decode_reduce_kernel: merge the partitions of sequences longer than one.
-//   grid = (q_heads, num_seqs), block = kReduceThreads; one workgroup per row.
+//   grid = (q_heads, num_seqs, D/DC), block = kReduceThreads; one workgroup
+//   per DC output dims of a row.
 //   out = Σ_p 2^(m_p − M) o_p / Σ_p 2^(m_p − M) l_p with M = max_p m_p.
-//   The per-partition weights 2^(m_p − M) are computed once into LDS (up to
-//   kReduceLds partitions; beyond that they are recomputed on the fly), then
-//   kReduceThreads/D partition lanes per output element accumulate it with
-//   loads coalesced over d.
+//   Each workgroup computes the per-partition weights 2^(m_p − M) into LDS
+//   (up to kReduceLds partitions; beyond that they are recomputed on the
+//   fly), then kReduceThreads/DC partition lanes per output element
+//   accumulate its DC dims.  Few rows (a long-context batch) take DC = 16, so
+//   a row's partitions are walked by 32 lanes in 8 workgroups instead of by
+//   4 lanes in one.
 // ---------------------------------------------------------------------------
 constexpr int kReduceThreads = 512;
 constexpr int kReduceLds = 4096;
+constexpr int kReduceSplitRows = 256;   // below this many rows the dims are split
 
 __device__ __forceinline__ float block_reduce_max(float v, float* sh /*[8]*/) {
 #pragma unroll
@@ -885,16 +905,18 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* sh /*[8]*/) {
   return r;
 }
 
-template <int D>
+template <int D, int DC>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __restrict__ out, int32_t out_dtype,
                                                                        const float* __restrict__ part_ml,
                                                                        const float* __restrict__ part_o,
                                                                        const int32_t* __restrict__ context_lens,
                                                                        int32_t q_heads, int32_t max_parts,
                                                                        int32_t part_tokens, int32_t max_ctx) {
-  constexpr int LANES = kReduceThreads / D;   // partition lanes per output element
+  constexpr int LANES = kReduceThreads / DC;   // partition lanes per output element
+  static_assert(D % DC == 0 && kReduceThreads % DC == 0, "dims split");
   const int s = blockIdx.y;
   const int h = blockIdx.x;
+  const int d0 = blockIdx.z * DC;
   const int tid = threadIdx.x;
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
@@ -907,7 +929,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
 
   __shared__ float sh_red[kReduceThreads / 64];
   __shared__ float sh_w[kReduceLds];
-  __shared__ float sh_acc[LANES][D];
+  __shared__ float sh_acc[LANES][DC];
   float mm = kNegBig;
   for (int p = tid; p < nparts; p += kReduceThreads) mm = fmaxf(mm, ml[2 * p]);
   const float M = block_reduce_max(mm, sh_red);
@@ -918,8 +940,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
     part += ml[2 * p + 1] * wgt;   // a NaN sum marks a partition that met a bad block id
   }
   const float L = block_reduce_sum(part, sh_red);   // its barriers also publish sh_w
-  const int d = tid % D;
-  const int pl = tid / D;
+  const int dl = tid % DC;
+  const int d = d0 + dl;
+  const int pl = tid / DC;
   // four independent accumulators keep four loads in flight per thread
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   int p = pl;
@@ -935,12 +958,12 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
     const float wgt = p < kReduceLds ? sh_w[p] : exp2f_fast(ml[2 * p] - M);
     acc[0] = __builtin_fmaf(wgt, po[static_cast<int64_t>(p) * D + d], acc[0]);
   }
-  sh_acc[pl][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  sh_acc[pl][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (pl == 0) {
     float O = 0.f;
 #pragma unroll
-    for (int k = 0; k < LANES; ++k) O += sh_acc[k][d];
+    for (int k = 0; k < LANES; ++k) O += sh_acc[k][dl];
     const float x = bad_len ? qnan() : (L > 0.f ? O / L : (L != L ? qnan() : 0.f));
     store_out(out, out_dtype, row * D + d, x);
   }
@@ -1310,9 +1333,16 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
                      a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3(a.q_heads, a.num_seqs), dim3(kReduceThreads), 0, stream, a.out,
-                     a.out_dtype, a.part_ml, a.part_o, a.context_lens, a.q_heads, a.max_parts,
-                     a.partition_tokens, a.max_context_len);
+  // fewer rows than CUs: split each row's dims over D/16 workgroups
+  if (static_cast<int64_t>(a.q_heads) * a.num_seqs < kReduceSplitRows) {
+    hipLaunchKernelGGL((decode_reduce_kernel<D, 16>), dim3(a.q_heads, a.num_seqs, D / 16), dim3(kReduceThreads), 0,
+                       stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, a.q_heads, a.max_parts,
+                       a.partition_tokens, a.max_context_len);
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<D, D>), dim3(a.q_heads, a.num_seqs, 1), dim3(kReduceThreads), 0, stream,
+                       a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, a.q_heads, a.max_parts,
+                       a.partition_tokens, a.max_context_len);
+  }
   return hipGetLastError();
 }
 

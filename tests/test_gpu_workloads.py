@@ -70,8 +70,9 @@ def _sample(ids, lens, k, seed):
     return sorted(picks)
 
 
-def run_step(pk, name, cow_step=False, samples=6):
-    """One decode step of workload ``name`` on the GPU, checked against the oracle."""
+def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None):
+    """One decode step of workload ``name`` on the GPU, checked against the
+    oracle (``partition_tokens`` overrides the workload's split)."""
     import torch
     w = WORKLOADS[name]
     sc = make_scenario(w)
@@ -105,7 +106,7 @@ def run_step(pk, name, cow_step=False, samples=6):
         pk.copy_blocks(pool, torch.tensor(pairs, dtype=torch.int32, device="cuda"))
     pk.write_kv(pool, k_new, v_new, torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda())
     out = pk.decode(pool, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), max_len,
-                    partition_tokens=w.partition_tokens)
+                    partition_tokens=w.partition_tokens if partition_tokens is None else partition_tokens)
     torch.cuda.synchronize()
 
     # pool bytes after the step: oracle copy + write on the host copy of the start state
@@ -172,6 +173,13 @@ def test_mha7b_fp16_full(gpu):
 
 def test_gqa70b_bf16_full(gpu):
     run_step(gpu, "gqa70b_bf16")
+
+
+@pytest.mark.parametrize("partition", [512, -1])
+def test_gqa70b_bf16_split_full(gpu, partition):
+    """The GQA batch split into 512-token partitions (16384 rows for the
+    reduce kernel, one workgroup per row) and by the balanced split."""
+    run_step(gpu, "gqa70b_bf16", partition_tokens=partition)
 
 
 def test_prefix_share_cow_step_full(gpu):
