@@ -200,6 +200,45 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
                     int32_t max_context_len, float scale, int32_t partition_tokens,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Sharing-aware decode ([P2] §3.4 and [P1] "跨请求的内存共享": forked samples
+ * and beams point their tables at the same physical blocks).  The result is
+ * pa_decode's (within fp32 rounding order), for a batch arranged in groups
+ * whose members hold their first tokens in the same blocks: each group's
+ * prefix is read once per kv-head for all members (the members' query rows
+ * share one matrix-core tile), each member's remaining tokens are read as
+ * usual, and the two partial softmaxes are merged by running max and sum
+ * ([P2] §4.1).
+ *   Arguments up to scale are pa_decode's.
+ *   num_groups ≥ 0; group_start: device int32[num_groups + 1], group k is
+ *     batch positions [group_start[k], group_start[k+1]), from 0 to num_seqs.
+ *   prefix_tokens: device int32[num_seqs]; for a member of group k the same
+ *     value P_k, a multiple of block_size, ≤ every member's length and
+ *     ≤ max_prefix_tokens, such that every member's first P_k / block_size
+ *     table entries equal those of the group's first member (0: no prefix).
+ *     pa_bm_prefix_groups computes groups and prefixes for a batch.
+ *   max_group_size: host bound on group sizes; max_prefix_tokens: host bound
+ *     on prefix_tokens (≤ max_context_len).
+ *   partition_tokens: > 0 fixed partitions (a multiple of block_size) for
+ *     prefixes and the rest; 0 = whole contexts when the batch fills the
+ *     device, else 512.  PA_PARTITION_BALANCED is rejected.
+ *   workspace: ≥ pa_decode_shared_prefix_workspace_bytes(...) bytes, 256-byte
+ *     aligned (partial results; no zero-fill needed).
+ * Pools with fp32 K/V or blocks under 16 tokens, and max_prefix_tokens = 0,
+ * take pa_decode itself (the grouping arguments are then ignored).  A
+ * violated grouping contract gives wrong rows, never an out-of-bounds
+ * access; PA_DEBUG_VALIDATE=1 checks it on the host.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
+pa_status pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
+                                                  int32_t max_context_len, int32_t max_prefix_tokens,
+                                                  int32_t partition_tokens, int64_t* bytes);
+pa_status pa_decode_shared_prefix(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q,
+                                  int32_t num_seqs, int32_t q_heads, const int32_t* block_tables,
+                                  int32_t block_table_stride, const int32_t* context_lens, int32_t max_context_len,
+                                  float scale, int32_t num_groups, const int32_t* group_start,
+                                  const int32_t* prefix_tokens, int32_t max_group_size, int32_t max_prefix_tokens,
+                                  int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block manager ([P2] §3.2, §3.3, §3.4; [P1] "跨请求的内存共享")        */
 /* Pure host code: needs no GPU.  Not thread-safe per instance.              */
@@ -293,6 +332,18 @@ pa_status pa_bm_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32
  * first.  Duplicate ids are allowed (each position is placed once).
  * Errors: PA_ERR_INVALID, PA_ERR_NOT_FOUND. */
 pa_status pa_bm_dispatch_order(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* order);
+
+/* Prefix groups of a decode batch for pa_decode_shared_prefix.  Runs of
+ * consecutive batch positions whose first block is the same physical block
+ * form the groups (arrange the batch with pa_bm_dispatch_order first);
+ * group_start (host int32[n + 1]) receives their starts and n, *num_groups
+ * their count, *max_group_size the largest.  prefix_tokens (host int32[n])
+ * receives, for each member, block_size × the number of leading table
+ * entries all members of its group share, counting only blocks that are
+ * full in every member; a group of one gets 0.
+ * Errors: PA_ERR_INVALID, PA_ERR_NOT_FOUND. */
+pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* group_start,
+                              int32_t* prefix_tokens, int32_t* num_groups, int32_t* max_group_size);
 
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc);
 

@@ -220,6 +220,34 @@ class OracleBlockManager:
                 keys.append((-longest, min(positions), -self.seqs[seq_ids[p]].length, p))
         return [k[3] for k in sorted(keys)]
 
+    def prefix_groups(self, seq_ids):
+        """Runs of consecutive batch positions whose first block is the same
+        physical block, and for each member the number of leading tokens held
+        in blocks that every member of its run shares and that are full in
+        every member (0 for a run of one).  Returns (starts + [n], prefix
+        tokens per position, largest run)."""
+        n = len(seq_ids)
+        seqs = [self.seqs[s] for s in seq_ids]
+        starts, prefix, largest = [], [0] * n, 0
+        a = 0
+        while a < n:
+            b = a + 1
+            if seqs[a].table:
+                while b < n and seqs[b].table and seqs[b].table[0] == seqs[a].table[0]:
+                    b += 1
+            blocks = 0
+            if b - a > 1:
+                limit = min(seq.length // self.block_size for seq in seqs[a:b])
+                while (blocks < limit and
+                       all(blocks < len(seq.table) and seq.table[blocks] == seqs[a].table[blocks] for seq in seqs[a:b])):
+                    blocks += 1
+            starts.append(a)
+            for i in range(a, b):
+                prefix[i] = blocks * self.block_size
+            largest = max(largest, b - a)
+            a = b
+        return starts + [n], prefix, largest
+
     def padded_tables(self, seq_ids, stride, pad=-1):
         """Block tables of ``seq_ids`` as rows of ``stride`` entries, padded with ``pad``."""
         rows = []

@@ -7,7 +7,9 @@ falls back to another implementation.
 """
 from ._lib import PaError, NoBlocksError, LIB_PATH, lib, PA_PARTITION_BALANCED
 from .api import (Pool, BlockManager, write_kv, copy_blocks, decode, decode_workspace_bytes,
-                  decode_partition_tokens, torch_dtype, dtype_name)
+                  decode_partition_tokens, decode_shared_prefix, decode_shared_prefix_workspace_bytes, torch_dtype,
+                  dtype_name)
 
-__all__ = ["PaError", "NoBlocksError", "LIB_PATH", "lib", "PA_PARTITION_BALANCED", "Pool", "BlockManager", "write_kv", "copy_blocks",
-           "decode", "decode_workspace_bytes", "decode_partition_tokens", "torch_dtype", "dtype_name"]
+__all__ = ["PaError", "NoBlocksError", "LIB_PATH", "lib", "PA_PARTITION_BALANCED", "Pool", "BlockManager", "write_kv",
+           "copy_blocks", "decode", "decode_workspace_bytes", "decode_partition_tokens", "decode_shared_prefix",
+           "decode_shared_prefix_workspace_bytes", "torch_dtype", "dtype_name"]

@@ -49,6 +49,9 @@ SIGNATURES = {
     "pa_decode_partition_tokens": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_p]),
     "pa_decode": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_i32, c_p, c_i32, c_p, c_i32, ctypes.c_float, c_i32,
                           c_p, c_i64, c_p]),
+    "pa_decode_shared_prefix_workspace_bytes": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p]),
+    "pa_decode_shared_prefix": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_i32, c_p, c_i32, c_p, c_i32, ctypes.c_float,
+                                        c_i32, c_p, c_p, c_i32, c_i32, c_i32, c_p, c_i64, c_p]),
     "pa_bm_create": (c_i32, [c_i32, c_i32, c_p, c_p]),
     "pa_bm_destroy": (None, [c_p]),
     "pa_bm_add_seq": (c_i32, [c_p, c_i64, c_i32]),
@@ -60,6 +63,7 @@ SIGNATURES = {
     "pa_bm_token_slots": (c_i32, [c_p, c_i64, c_i32, c_i32, c_p]),
     "pa_bm_tables": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_p]),
     "pa_bm_dispatch_order": (c_i32, [c_p, c_p, c_i32, c_p]),
+    "pa_bm_prefix_groups": (c_i32, [c_p, c_p, c_i32, c_p, c_p, c_p, c_p]),
     "pa_bm_refcount": (c_i32, [c_p, c_i32, c_p]),
     "pa_bm_free_list": (c_i32, [c_p, c_p, c_i32, c_p]),
     "pa_bm_stats": (c_i32, [c_p, c_p]),

@@ -144,6 +144,50 @@ def decode(pool, q, block_tables, context_lens, max_context_len, out=None, out_d
     return out
 
 
+def decode_shared_prefix_workspace_bytes(pool, num_seqs, q_heads, max_context_len, max_prefix_tokens,
+                                         partition_tokens=0):
+    """Workspace bytes ``decode_shared_prefix`` needs."""
+    out = ctypes.c_int64()
+    check(lib().pa_decode_shared_prefix_workspace_bytes(pool.handle, num_seqs, q_heads, max_context_len,
+                                                        max_prefix_tokens, partition_tokens, ctypes.addressof(out)),
+          "pa_decode_shared_prefix_workspace_bytes")
+    return out.value
+
+
+def decode_shared_prefix(pool, q, block_tables, context_lens, max_context_len, group_start, prefix_tokens,
+                         max_group_size, max_prefix_tokens, out=None, out_dtype=None, scale=None, partition_tokens=0,
+                         workspace=None, stream=None):
+    """Sharing-aware paged decode (each group's common prefix read once per
+    kv-head); ``group_start`` [num_groups + 1] and ``prefix_tokens``
+    [num_seqs] are int32 device tensors (see ``BlockManager.prefix_groups``)."""
+    import torch
+    num_seqs, q_heads, d = (int(x) for x in q.shape)
+    if d != pool.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    tdt = torch_dtype(pool.dtype)
+    odt = out_dtype or pool.dtype
+    if out is None:
+        out = torch.empty((num_seqs, q_heads, d), dtype=torch_dtype(odt), device=q.device)
+    ws_bytes = decode_shared_prefix_workspace_bytes(pool, num_seqs, q_heads, max_context_len, max_prefix_tokens,
+                                                    partition_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stride = int(block_tables.shape[1]) if block_tables.dim() == 2 else 0
+    num_groups = int(group_start.numel()) - 1
+    check(lib().pa_decode_shared_prefix(
+        pool.handle, _dev_ptr(out, "out", torch_dtype(odt), (num_seqs, q_heads, d)), DTYPE_CODES[odt],
+        _dev_ptr(q, "q", tdt), num_seqs, q_heads, _dev_ptr(block_tables, "block_tables", torch.int32), stride,
+        _dev_ptr(context_lens, "context_lens", torch.int32, (num_seqs,)), int(max_context_len),
+        float(scale) if scale else 0.0, num_groups,
+        _dev_ptr(group_start, "group_start", torch.int32, (num_groups + 1,)) if num_groups > 0 else None,
+        _dev_ptr(prefix_tokens, "prefix_tokens", torch.int32, (num_seqs,)) if num_groups > 0 else None,
+        int(max_group_size), int(max_prefix_tokens), int(partition_tokens), ws_ptr, ws_len, _stream(stream)),
+        "pa_decode_shared_prefix")
+    return out
+
+
 # ----------------------------------------------------------------------------
 # host block manager
 # ----------------------------------------------------------------------------
@@ -241,6 +285,18 @@ class BlockManager:
         check(lib().pa_bm_dispatch_order(self.handle, ids.ctypes.data, ids.shape[0], order.ctypes.data),
               "pa_bm_dispatch_order")
         return order[:ids.shape[0]]
+
+    def prefix_groups(self, seq_ids):
+        """(group_start int32[num_groups + 1], prefix_tokens int32[n],
+        max_group_size) of a batch for ``decode_shared_prefix``."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        starts = np.empty(n + 1, dtype=np.int32)
+        prefix = np.empty(max(n, 1), dtype=np.int32)
+        ng, mg = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().pa_bm_prefix_groups(self.handle, ids.ctypes.data, n, starts.ctypes.data, prefix.ctypes.data,
+                                        ctypes.addressof(ng), ctypes.addressof(mg)), "pa_bm_prefix_groups")
+        return starts[:ng.value + 1].copy(), prefix[:n].copy(), mg.value
 
     def refcount(self, block):
         rc = ctypes.c_int32()

@@ -147,6 +147,60 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
   return PA_OK;
 }
 
+// The shared-prefix call's split: fixed partitions always (its prefix pass
+// and the suffix pass write partial records that decode_reduce_kernel
+// merges).  partition_tokens > 0 is used as given; 0 picks whole contexts
+// when the batch's (sequence, kv-head) units fill the device, else 512
+// tokens.  max_parts = prefix partitions + context partitions.
+pa_status plan_shared_prefix(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
+                             int32_t max_prefix, int32_t requested, DecodePlan* plan) {
+  const pa::PoolDesc& d = pool->d;
+  if (requested < 0) return fail(PA_ERR_INVALID, "partition_tokens must be >= 0 for a shared-prefix decode");
+  if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
+                                        " (q_heads must be kv_heads x 1, 2, 4 or 8)");
+  *plan = DecodePlan{};
+  int32_t p = requested;
+  if (p == 0) {
+    int32_t grid = 0, capacity = 0;
+    hipError_t e = pa::decode_balanced_grid(d, q_heads / d.kv_heads, num_seqs, max_context_len, &grid, &capacity);
+    if (e != hipSuccess) return hip_fail(e, "decode grid query");
+    const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
+    p = units >= capacity ? static_cast<int32_t>(ceil_div(std::max(max_context_len, 1), d.block_size) * d.block_size)
+                          : 512;
+  }
+  if (p % d.block_size != 0)
+    return fail(PA_ERR_INVALID, "partition_tokens must be a positive multiple of block_size (" +
+                                    std::to_string(d.block_size) + ")");
+  plan->partition_tokens = p;
+  plan->max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_prefix, p) + ceil_div(max_context_len, p)));
+  const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts;
+  plan->ml_off = 0;
+  plan->o_off = round256(rows * 2 * 4);
+  plan->bytes = plan->o_off + rows * d.head_dim * 4;
+  return PA_OK;
+}
+
+// Host checks of pa_decode's device-resident indices (PA_DEBUG_VALIDATE).
+pa_status validate_decode_indices(const pa::PoolDesc& d, int32_t num_seqs, const int32_t* block_tables,
+                                  int32_t stride, const int32_t* context_lens, int32_t max_context_len,
+                                  hipStream_t st, std::vector<int32_t>* lens, std::vector<int32_t>* tables) {
+  if (pa_status s = fetch_ints(context_lens, num_seqs, lens, st)) return s;
+  if (pa_status s = fetch_ints(block_tables, static_cast<int64_t>(num_seqs) * stride, tables, st)) return s;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if ((*lens)[i] < 0 || (*lens)[i] > max_context_len)
+      return fail(PA_ERR_INVALID, "context_lens[" + std::to_string(i) + "] outside [0, max_context_len]");
+    const int64_t nblk = ceil_div((*lens)[i], d.block_size);
+    for (int64_t j = 0; j < nblk; ++j) {
+      const int32_t b = (*tables)[static_cast<size_t>(i) * stride + j];
+      if (b < 0 || b >= d.num_blocks)
+        return fail(PA_ERR_INVALID, "block_tables[" + std::to_string(i) + "][" + std::to_string(j) + "] = " +
+                                        std::to_string(b) + " outside the pool");
+    }
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,20 +377,9 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (debug_validate()) {
     std::vector<int32_t> lens, tables;
-    if (pa_status s = fetch_ints(context_lens, num_seqs, &lens, st)) return s;
-    if (pa_status s = fetch_ints(block_tables, static_cast<int64_t>(num_seqs) * block_table_stride, &tables, st))
+    if (pa_status s = validate_decode_indices(d, num_seqs, block_tables, block_table_stride, context_lens,
+                                              max_context_len, st, &lens, &tables))
       return s;
-    for (int32_t i = 0; i < num_seqs; ++i) {
-      if (lens[i] < 0 || lens[i] > max_context_len)
-        return fail(PA_ERR_INVALID, "context_lens[" + std::to_string(i) + "] outside [0, max_context_len]");
-      const int64_t nblk = ceil_div(lens[i], d.block_size);
-      for (int64_t j = 0; j < nblk; ++j) {
-        const int32_t b = tables[static_cast<size_t>(i) * block_table_stride + j];
-        if (b < 0 || b >= d.num_blocks)
-          return fail(PA_ERR_INVALID, "block_tables[" + std::to_string(i) + "][" + std::to_string(j) + "] = " +
-                                          std::to_string(b) + " outside the pool");
-      }
-    }
     if (plan.balanced) {
       std::vector<int32_t> ctr;
       const int64_t n = int64_t{pa::kMergeLevels} * plan.num_slots;
@@ -377,6 +420,122 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
   }
   hipError_t e = pa::launch_decode(d, a, st);
   return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
+}
+
+pa_status pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
+                                                  int32_t max_context_len, int32_t max_prefix_tokens,
+                                                  int32_t partition_tokens, int64_t* bytes) {
+  if (!pool || !bytes) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (num_seqs < 0 || q_heads <= 0 || q_heads % pool->d.kv_heads != 0 || max_context_len < 0 ||
+      max_prefix_tokens < 0 || max_prefix_tokens > max_context_len)
+    return fail(PA_ERR_INVALID, "bad sizes");
+  *bytes = 0;
+  if (num_seqs == 0) return PA_OK;
+  if (!pa::shared_prefix_supported(pool->d.dtype, pool->d.block_size) || max_prefix_tokens == 0)
+    return pa_decode_workspace_bytes(pool, num_seqs, q_heads, max_context_len, partition_tokens, bytes);
+  DecodePlan plan;
+  if (pa_status s = plan_shared_prefix(pool, num_seqs, q_heads, max_context_len, max_prefix_tokens, partition_tokens,
+                                       &plan))
+    return s;
+  *bytes = plan.bytes;
+  return PA_OK;
+}
+
+pa_status pa_decode_shared_prefix(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q,
+                                  int32_t num_seqs, int32_t q_heads, const int32_t* block_tables,
+                                  int32_t block_table_stride, const int32_t* context_lens, int32_t max_context_len,
+                                  float scale, int32_t num_groups, const int32_t* group_start,
+                                  const int32_t* prefix_tokens, int32_t max_group_size, int32_t max_prefix_tokens,
+                                  int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  const pa::PoolDesc& d = pool->d;
+  if (num_groups < 0 || num_groups > num_seqs || max_prefix_tokens < 0 || max_prefix_tokens > max_context_len ||
+      max_group_size < 0 || max_group_size > std::max(num_seqs, 0))
+    return fail(PA_ERR_INVALID, "bad group sizes");
+  if (!pa::shared_prefix_supported(d.dtype, d.block_size) || max_prefix_tokens == 0)
+    return pa_decode(pool, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride, context_lens,
+                     max_context_len, scale, partition_tokens, workspace, workspace_bytes, stream);
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "num_seqs must be in [0, 65535]");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !context_lens) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (num_groups > 0 && (!group_start || !prefix_tokens || max_group_size < 1))
+    return fail(PA_ERR_INVALID, "group_start, prefix_tokens and max_group_size are needed with groups");
+  if (q_heads <= 0 || q_heads % d.kv_heads != 0)
+    return fail(PA_ERR_INVALID, "q_heads must be a positive multiple of kv_heads");
+  const int32_t group = q_heads / d.kv_heads;
+  if (out_dtype != d.dtype && out_dtype != PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "out_dtype must be the pool dtype or PA_F32");
+  if (d.kv_heads > 65535 || q_heads > 65535) return fail(PA_ERR_INVALID, "kv_heads and q_heads must be <= 65535");
+  const int64_t tiles = ceil_div(std::max(max_group_size, 1), 16 / group);
+  if (static_cast<int64_t>(d.kv_heads) * tiles > 65535)
+    return fail(PA_ERR_INVALID, "kv_heads x member tiles must be <= 65535");
+  if (block_table_stride < ceil_div(max_context_len, d.block_size))
+    return fail(PA_ERR_INVALID, "block_table_stride shorter than ceil(max_context_len / block_size)");
+  if (!aligned(q, 16)) return fail(PA_ERR_INVALID, "q must be 16-byte aligned");
+  DecodePlan plan;
+  if (pa_status s = plan_shared_prefix(pool, num_seqs, q_heads, max_context_len, max_prefix_tokens, partition_tokens,
+                                       &plan))
+    return s;
+  if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 256))
+    return fail(PA_ERR_INVALID,
+                "workspace must be 256-byte aligned and hold " + std::to_string(plan.bytes) + " bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_validate()) {
+    std::vector<int32_t> lens, tables, gs, pre;
+    if (pa_status s = validate_decode_indices(d, num_seqs, block_tables, block_table_stride, context_lens,
+                                              max_context_len, st, &lens, &tables))
+      return s;
+    if (num_groups > 0) {
+      if (pa_status s = fetch_ints(group_start, num_groups + 1, &gs, st)) return s;
+      if (pa_status s = fetch_ints(prefix_tokens, num_seqs, &pre, st)) return s;
+      if (gs[0] != 0 || gs[num_groups] != num_seqs)
+        return fail(PA_ERR_INVALID, "group_start must run from 0 to num_seqs");
+      for (int32_t k = 0; k < num_groups; ++k) {
+        const int32_t a = gs[k], b = gs[k + 1];
+        if (b < a) return fail(PA_ERR_INVALID, "group_start must not decrease");
+        if (b - a > max_group_size) return fail(PA_ERR_INVALID, "a group is larger than max_group_size");
+        for (int32_t i = a; i < b; ++i) {
+          const int32_t pi = pre[i];
+          if (pi != pre[a]) return fail(PA_ERR_INVALID, "prefix_tokens differ inside group " + std::to_string(k));
+          if (pi < 0 || pi % d.block_size != 0 || pi > lens[i] || pi > max_prefix_tokens)
+            return fail(PA_ERR_INVALID, "prefix_tokens[" + std::to_string(i) +
+                                            "] must be a multiple of block_size in [0, min(length, max_prefix)]");
+          for (int32_t j = 0; j < pi / d.block_size; ++j)
+            if (tables[static_cast<size_t>(i) * block_table_stride + j] !=
+                tables[static_cast<size_t>(a) * block_table_stride + j])
+              return fail(PA_ERR_INVALID, "sequence " + std::to_string(i) +
+                                              " does not hold its group's prefix in the same blocks");
+        }
+      }
+    }
+  }
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.block_tables = block_tables;
+  a.table_stride = block_table_stride;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d.head_dim));
+  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);  // log2(e)
+  a.partition_tokens = plan.partition_tokens;
+  a.max_parts = plan.max_parts;
+  char* ws = static_cast<char*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(ws + plan.ml_off);
+  a.part_o = reinterpret_cast<float*>(ws + plan.o_off);
+  if (num_groups > 0) {
+    a.group_start = group_start;
+    a.seq_prefix = prefix_tokens;
+    a.num_groups = num_groups;
+    a.max_group_size = max_group_size;
+    a.max_prefix = max_prefix_tokens;
+  }
+  hipError_t e = pa::launch_decode(d, a, st);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "shared-prefix decode launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -515,6 +674,15 @@ pa_status pa_bm_dispatch_order(const pa_bm* bm, const int64_t* seq_ids, int32_t 
   if (!bm || n < 0 || (n > 0 && (!seq_ids || !order))) return fail(PA_ERR_INVALID, "bad arguments");
   std::string why;
   return map_bm(bm->impl.dispatch_order(seq_ids, n, order, &why), why);
+}
+
+pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* group_start,
+                              int32_t* prefix_tokens, int32_t* num_groups, int32_t* max_group_size) {
+  if (!bm || n < 0 || !group_start || !num_groups || !max_group_size || (n > 0 && (!seq_ids || !prefix_tokens)))
+    return fail(PA_ERR_INVALID, "bad arguments");
+  std::string why;
+  return map_bm(bm->impl.prefix_groups(seq_ids, n, group_start, prefix_tokens, num_groups, max_group_size, &why),
+                why);
 }
 
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc) {

@@ -207,6 +207,44 @@ BmResult BlockManager::dispatch_order(const int64_t* ids, int32_t n, int32_t* or
   return BmResult::ok;
 }
 
+BmResult BlockManager::prefix_groups(const int64_t* ids, int32_t n, int32_t* group_start, int32_t* prefix_tokens,
+                                     int32_t* num_groups, int32_t* max_group_size, std::string* why) const {
+  std::vector<const Seq*> batch(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = seqs_.find(ids[i]);
+    if (it == seqs_.end()) {
+      *why = "unknown sequence " + std::to_string(ids[i]);
+      return BmResult::not_found;
+    }
+    batch[i] = &it->second;
+  }
+  int32_t groups = 0, largest = 0;
+  for (int32_t a = 0; a < n;) {
+    int32_t b = a + 1;
+    if (!batch[a]->table.empty())
+      while (b < n && !batch[b]->table.empty() && batch[b]->table.front() == batch[a]->table.front()) ++b;
+    int64_t blocks = 0;
+    if (b - a > 1) {
+      blocks = static_cast<int64_t>(batch[a]->table.size());
+      for (int32_t i = a; i < b; ++i) {
+        const std::vector<int32_t>& t = batch[i]->table;
+        blocks = std::min<int64_t>(blocks, batch[i]->length / block_size_);   // full blocks only
+        int64_t j = 0;
+        while (j < blocks && t[j] == batch[a]->table[j]) ++j;
+        blocks = j;
+      }
+    }
+    group_start[groups++] = a;
+    for (int32_t i = a; i < b; ++i) prefix_tokens[i] = static_cast<int32_t>(blocks * block_size_);
+    largest = std::max(largest, b - a);
+    a = b;
+  }
+  group_start[groups] = n;
+  *num_groups = groups;
+  *max_group_size = largest;
+  return BmResult::ok;
+}
+
 BmResult BlockManager::free_seq(int64_t id, std::string* why) {
   auto it = seqs_.find(id);
   if (it == seqs_.end()) {

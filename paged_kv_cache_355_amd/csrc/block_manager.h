@@ -46,6 +46,13 @@ class BlockManager {
   // sequences are singleton groups of length 0.  With no sharing this is a
   // stable sort by length, longest first.
   BmResult dispatch_order(const int64_t* ids, int32_t n, int32_t* order, std::string* why) const;
+  // Prefix groups of a decode batch: runs of consecutive positions whose
+  // first block is the same physical block.  group_start[num_groups + 1];
+  // prefix_tokens[n] = block_size × the leading table entries every member of
+  // the run holds in common, counting only blocks full in every member (0 for
+  // a run of one).
+  BmResult prefix_groups(const int64_t* ids, int32_t n, int32_t* group_start, int32_t* prefix_tokens,
+                         int32_t* num_groups, int32_t* max_group_size, std::string* why) const;
   BmResult free_seq(int64_t id, std::string* why);
 
   const std::vector<int32_t>* table(int64_t id, int32_t* length) const;

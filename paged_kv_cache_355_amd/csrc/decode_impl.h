@@ -325,12 +325,16 @@ __device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ b
   return shared;
 }
 
-template <int DT, int D, int BS, int G, int NW, bool STREAM, typename Emit>
+// R query rows (R ≤ 16) against kv-head g's tiles over tokens [t_begin,
+// t_end).  q_lane: the start of this lane's query row (row lane % 16), or
+// nullptr for a row past R or unused (it contributes zeros); q_dummy: any
+// valid, cache-resident address (read by the loads of chunks past the end).
+template <int DT, int D, int BS, int R, int NW, bool STREAM, typename Emit>
 __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
-                                                  const char* __restrict__ q, const int32_t* __restrict__ table,
-                                                  int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
-                                                  int32_t t_begin, int32_t t_end, float scale_log2,
-                                                  WaveMerge<NW, G, D, true>& sh, Emit&& emit) {
+                                                  const char* q_lane, const char* __restrict__ q_dummy,
+                                                  const int32_t* __restrict__ table, int32_t g, int32_t kv_heads,
+                                                  int32_t num_blocks, int32_t t_begin, int32_t t_end,
+                                                  float scale_log2, WaveMerge<NW, R, D, true>& sh, Emit&& emit) {
   constexpr int EB = 2;
   constexpr int ROW = D * EB;          // bytes per token row
   constexpr int CT = 16;               // tokens per chunk (the MFMA M dimension)
@@ -339,22 +343,22 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   constexpr int64_t TILE = static_cast<int64_t>(BS) * ROW;
   constexpr int LPR = ROW / 16;        // lanes per V row in a contiguous load
   constexpr int RPI = 64 / LPR;        // V rows per load instruction
-  static_assert(BS % CT == 0 && G <= 16, "matrix-core path needs 16-token tiles and ≤ 16 rows");
+  static_assert(BS % CT == 0 && R <= 16, "matrix-core path needs 16-token tiles and ≤ 16 rows");
   static_assert(RPI * NKL == CT, "NKL contiguous loads cover the 16-row V tile");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tl = lane & 15;   // token (K/V loads, S/P columns) or row (Q, O) of this lane
   const int qd = lane >> 4;   // quarter: dim slice of the loads, token group of S/P
-  const int q_heads = kv_heads * G;
 
-  // Qᵀ operand: row tl (zero for tl ≥ G), dims [32i + 8qd, +8)
-  const char* q_row = q + ((static_cast<int64_t>(s) * q_heads + g * G + min(tl, G - 1)) * D) * EB + qd * 16;
+  // Qᵀ operand: row tl (zero where q_lane is null), dims [32i + 8qd, +8)
+  const char* q_row = q_dummy + qd * 16;   // dead loads read here
+  const char* q_src = (q_lane ? q_lane : q_dummy) + qd * 16;
   uint4 qop[NKL];
 #pragma unroll
   for (int i = 0; i < NKL; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(q_row + i * 64);
-    qop[i] = tl < G ? v : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 v = *reinterpret_cast<const uint4*>(q_src + i * 64);
+    qop[i] = q_lane ? v : make_uint4(0u, 0u, 0u, 0u);
   }
   float m = kNegBig, l = 0.f;
   f32x4_t ob[NB];
@@ -500,7 +504,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   l += __shfl_xor(l, 32, 64);
 
   // Merge the NW waves through LDS and hand each output to emit.
-  if (tl < G) {
+  if (tl < R) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -517,7 +521,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   bool bad = false;
 #pragma unroll
   for (int w = 0; w < NW; ++w) bad = bad || sh.bad[w] != 0;
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+  for (int idx = threadIdx.x; idx < R * D; idx += NW * 64) {
     const int r = idx / D;
     const int d = idx - r * D;
     float mm = kNegBig;
@@ -561,8 +565,11 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
                                              int32_t t_begin, int32_t t_end, float scale_log2,
                                              WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
   if constexpr (kUseMfma<DT, BS, G>) {
-    attend_range_mfma<DT, D, BS, G, NW, STREAM>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin,
-                                                t_end, scale_log2, sh, emit);
+    constexpr int EB = 2;
+    const int tl = threadIdx.x & 15;
+    const char* q_head0 = q + ((static_cast<int64_t>(s) * kv_heads * G + g * G) * D) * EB;   // row g·G of sequence s
+    attend_range_mfma<DT, D, BS, G, NW, STREAM>(k_pool, v_pool, tl < G ? q_head0 + tl * D * EB : nullptr, q_head0,
+                                                table, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh, emit);
     return;
   } else {
   using S = Shape<DT, D>;
@@ -782,6 +789,24 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
   }
 }
 
+// Tokens at the start of sequence s that a shared-prefix call computes in its
+// group's prefix pass: seq_prefix[s] clamped to [0, min(len, max_prefix)]
+// and rounded down to a whole number of blocks (0 without seq_prefix).  The
+// partition, prefix and reduce kernels all derive it this way, so they agree
+// on every row's partial records.
+template <int BS>
+__device__ __forceinline__ int32_t prefix_of(const int32_t* __restrict__ seq_prefix, int32_t s, int32_t len,
+                                             int32_t max_prefix) {
+  if (!seq_prefix) return 0;
+  const int32_t p = min(max(seq_prefix[s], 0), min(len, max_prefix));
+  return p - p % BS;
+}
+
+// Partitions of part_tokens covering n ≥ 0 tokens.
+__device__ __forceinline__ int32_t parts_of(int32_t n, int32_t part_tokens) {
+  return n <= 0 ? 0 : (n + part_tokens - 1) / part_tokens;
+}
+
 // Write zero rows (an empty context) or NaN rows (an invalid length) for all
 // query heads of kv-head range [g0, g1) of sequence s.
 template <int D, int G>
@@ -827,8 +852,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
-    int32_t num_seqs, int32_t num_blocks, int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens,
-    float scale_log2) {
+    const int32_t* __restrict__ seq_prefix, int32_t max_prefix, int32_t num_seqs, int32_t num_blocks,
+    int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2) {
   const int p = blockIdx.x;
   const int g = blockIdx.y;
   const int s = blockIdx.z;
@@ -837,25 +862,31 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
-  const int32_t nparts = len_c <= part_tokens ? 1 : (len_c + part_tokens - 1) / part_tokens;
-  if (p >= nparts) return;
   if (len_c == 0) {
-    fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
+    if (p == 0) fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
     return;
   }
-  const int32_t t_begin = p * part_tokens;
+  // With a shared prefix this workgroup covers part p of the suffix; the
+  // prefix's npp partials come from decode_prefix_kernel.
+  const int32_t pre = prefix_of<BS>(seq_prefix, s, len_c, max_prefix);
+  const int32_t npp = parts_of(pre, part_tokens);
+  const int32_t nsp = parts_of(len_c - pre, part_tokens);
+  if (p >= nsp) return;
+  const int32_t nparts = npp + nsp;
+  const int32_t t_begin = pre + p * part_tokens;
   const int32_t t_end = min(t_begin + part_tokens, len_c);
   const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
   __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
+  // after a prefix pass the tiles read here are this sequence's own
+  const bool shared = pre == 0 && shares_first_block(block_tables, table_stride, s, num_seqs);
   attend_range_policy<DT, D, BS, G, NW>(
-      shares_first_block(block_tables, table_stride, s, num_seqs), k_pool, v_pool, q, table, s, g, kv_heads,
-      num_blocks, t_begin, t_end, scale_log2, sh,
+      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
         if (nparts == 1) {
           store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
         } else {
-          const int64_t prow = row * max_parts + p;
+          const int64_t prow = row * max_parts + npp + p;
           part_o[prow * D + d] = bad ? qnan() : O;
           if (d == 0) {
             part_ml[2 * prow] = M;
@@ -866,9 +897,78 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
 }
 
 // ---------------------------------------------------------------------------
+// decode_prefix_kernel: the shared prefix of a group of sequences, read once
+// per kv-head for every member ([P2] §3.4; [P1] "跨请求的内存共享": the
+// members' tables point at the same physical blocks, so the tokens there
+// are the same for all of them).
+//   grid = (prefix partitions, kv_heads × member tiles, groups).
+//   Group k is batch positions [group_start[k], group_start[k+1]); its
+//   prefix is prefix_of(first member of the tile).  A member tile is 16/G
+//   members, whose G query rows per kv-head fill the 16 rows of the
+//   matrix-core tile, so K·Qᵀ and P·V serve all of them at once.  Each
+//   writes the (max, sum, output) partial of prefix partition pp of every
+//   row it holds as that row's part pp; the partition kernel adds the
+//   suffix's parts after them and decode_reduce_kernel merges.
+//   Tiles of one (group, kv-head) are kv_heads workgroups apart, so with
+//   kv_heads a multiple of 8 they run on one XCD and share its L2; a group
+//   held in one tile streams its prefix.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_prefix_kernel(
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
+    float* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ block_tables,
+    int32_t table_stride, const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ seq_prefix, int32_t max_prefix, int32_t num_seqs, int32_t num_blocks,
+    int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2) {
+  constexpr int MT = 16 / G;   // members per tile
+  constexpr int EB = 2;
+  const int pp = blockIdx.x;
+  const int g = blockIdx.y % kv_heads;
+  const int mt = blockIdx.y / kv_heads;
+  // clamped, so a malformed group list yields wrong rows, never a stray access
+  const int32_t m_begin = min(max(group_start[blockIdx.z], 0), num_seqs);
+  const int32_t m_end = min(max(group_start[blockIdx.z + 1], m_begin), num_seqs);
+  const int32_t m0 = m_begin + mt * MT;
+  if (m0 >= m_end) return;
+  const int32_t m1 = min(m0 + MT, m_end);
+  const int32_t len0 = context_lens[m0];
+  const int32_t pre = prefix_of<BS>(seq_prefix, m0, (len0 < 0 || len0 > max_ctx) ? 0 : len0, max_prefix);
+  if (pp >= parts_of(pre, part_tokens)) return;
+  const int32_t t_begin = pp * part_tokens;
+  const int32_t t_end = min(t_begin + part_tokens, pre);
+  const int q_heads = kv_heads * G;
+
+  const int tl = threadIdx.x & 15;
+  const int32_t member = m0 + tl / G;
+  const char* q_dummy = q + ((static_cast<int64_t>(m0) * q_heads + g * G) * D) * EB;
+  const char* q_lane =
+      member < m1 ? q + ((static_cast<int64_t>(member) * q_heads + g * G + tl % G) * D) * EB : nullptr;
+  const int32_t* table = block_tables + static_cast<int64_t>(m0) * table_stride;
+  __shared__ WaveMerge<NW, 16, D, true> sh;
+  auto emit = [&](int r, int d, float M, float L, float O, bool bad) {
+    const int32_t mem = m0 + r / G;
+    if (mem >= m1) return;
+    const int64_t prow = (static_cast<int64_t>(mem) * q_heads + g * G + r % G) * max_parts + pp;
+    part_o[prow * D + d] = bad ? qnan() : O;
+    if (d == 0) {
+      part_ml[2 * prow] = M;
+      part_ml[2 * prow + 1] = L;
+    }
+  };
+  if (m_end - m_begin <= MT) {
+    attend_range_mfma<DT, D, BS, 16, NW, true>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
+                                               t_begin, t_end, scale_log2, sh, emit);
+  } else {
+    attend_range_mfma<DT, D, BS, 16, NW, false>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
+                                                t_begin, t_end, scale_log2, sh, emit);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // decode_reduce_kernel: merge the partitions of sequences longer than one.
 //   grid = (q_heads, num_seqs, D/DC), block = kReduceThreads; one workgroup
-//   per DC output dims of a row.
+//   per DC output dims of a row.  With a shared prefix a row's parts are the
+//   prefix's partials followed by the suffix's.
 //   out = Σ_p 2^(m_p − M) o_p / Σ_p 2^(m_p − M) l_p with M = max_p m_p.
 //   Each workgroup computes the per-partition weights 2^(m_p − M) into LDS
 //   (up to kReduceLds partitions; beyond that they are recomputed on the
@@ -905,13 +1005,15 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* sh /*[8]*/) {
   return r;
 }
 
-template <int D, int DC>
+template <int D, int DC, int BS>
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __restrict__ out, int32_t out_dtype,
                                                                        const float* __restrict__ part_ml,
                                                                        const float* __restrict__ part_o,
                                                                        const int32_t* __restrict__ context_lens,
-                                                                       int32_t q_heads, int32_t max_parts,
-                                                                       int32_t part_tokens, int32_t max_ctx) {
+                                                                       const int32_t* __restrict__ seq_prefix,
+                                                                       int32_t max_prefix, int32_t q_heads,
+                                                                       int32_t max_parts, int32_t part_tokens,
+                                                                       int32_t max_ctx) {
   constexpr int LANES = kReduceThreads / DC;   // partition lanes per output element
   static_assert(D % DC == 0 && kReduceThreads % DC == 0, "dims split");
   const int s = blockIdx.y;
@@ -921,8 +1023,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
-  const int32_t nparts = len_c <= part_tokens ? 1 : (len_c + part_tokens - 1) / part_tokens;
-  if (nparts == 1) return;  // written by the partition kernel (NaN rows included)
+  const int32_t pre = prefix_of<BS>(seq_prefix, s, len_c, max_prefix);
+  const int32_t nparts = parts_of(pre, part_tokens) + parts_of(len_c - pre, part_tokens);
+  if (len_c == 0 || (pre == 0 && nparts == 1)) return;  // written by the partition kernel (NaN rows included)
   const int64_t row = static_cast<int64_t>(s) * q_heads + h;
   const float* ml = part_ml + row * max_parts * 2;
   const float* po = part_o + row * max_parts * D;
@@ -1325,23 +1428,43 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
                        a.scale_log2);
     return hipGetLastError();
   }
+  const bool shared_prefix = a.group_start != nullptr && a.num_groups > 0 && a.max_prefix > 0;
+  if (shared_prefix) {
+    if constexpr (DT != kF32 && BS >= 16) {
+      const int32_t tiles = (a.max_group_size + 16 / G - 1) / (16 / G);
+      const int32_t prefix_parts = (a.max_prefix + a.partition_tokens - 1) / a.partition_tokens;
+      hipLaunchKernelGGL((decode_prefix_kernel<DT, D, BS, G, kWaves>),
+                         dim3(prefix_parts, p.kv_heads * tiles, a.num_groups), dim3(kThreads), 0, stream,
+                         static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
+                         a.part_ml, a.part_o, a.block_tables, a.table_stride, a.context_lens, a.group_start,
+                         a.seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len,
+                         a.max_parts, a.partition_tokens, a.scale_log2);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      return hipErrorInvalidValue;   // the host takes the plain path for these pools
+    }
+  }
+  const int32_t* seq_prefix = shared_prefix ? a.seq_prefix : nullptr;
+  // suffix partitions: at most max_parts minus the prefix's (the host sizes
+  // max_parts as prefix parts + context parts, so this covers every suffix)
   dim3 grid(a.max_parts, p.kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
-                     a.table_stride, a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len,
-                     a.max_parts, a.partition_tokens, a.scale_log2);
+                     a.table_stride, a.context_lens, seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads,
+                     a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   // fewer rows than CUs: split each row's dims over D/16 workgroups
   if (static_cast<int64_t>(a.q_heads) * a.num_seqs < kReduceSplitRows) {
-    hipLaunchKernelGGL((decode_reduce_kernel<D, 16>), dim3(a.q_heads, a.num_seqs, D / 16), dim3(kReduceThreads), 0,
-                       stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, a.q_heads, a.max_parts,
-                       a.partition_tokens, a.max_context_len);
+    hipLaunchKernelGGL((decode_reduce_kernel<D, 16, BS>), dim3(a.q_heads, a.num_seqs, D / 16), dim3(kReduceThreads),
+                       0, stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, seq_prefix, a.max_prefix,
+                       a.q_heads, a.max_parts, a.partition_tokens, a.max_context_len);
   } else {
-    hipLaunchKernelGGL((decode_reduce_kernel<D, D>), dim3(a.q_heads, a.num_seqs, 1), dim3(kReduceThreads), 0, stream,
-                       a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, a.q_heads, a.max_parts,
-                       a.partition_tokens, a.max_context_len);
+    hipLaunchKernelGGL((decode_reduce_kernel<D, D, BS>), dim3(a.q_heads, a.num_seqs, 1), dim3(kReduceThreads), 0,
+                       stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, seq_prefix, a.max_prefix,
+                       a.q_heads, a.max_parts, a.partition_tokens, a.max_context_len);
   }
   return hipGetLastError();
 }

@@ -48,7 +48,22 @@ struct DecodeArgs {
   // balanced: [num_slots][group] rows.
   float* part_ml;          // rows × (max, sum)
   float* part_o;           // rows × head_dim
+  // Shared prefixes (fixed partitions only; all null/0 for plain decode):
+  // group k is batch positions [group_start[k], group_start[k+1]) whose first
+  // seq_prefix tokens sit in the same physical blocks.  max_parts then counts
+  // the prefix's partitions plus the context's.
+  const int32_t* group_start = nullptr;   // device [num_groups + 1]
+  const int32_t* seq_prefix = nullptr;    // device [num_seqs]
+  int32_t num_groups = 0;
+  int32_t max_group_size = 0;
+  int32_t max_prefix = 0;
 };
+
+// True when the shared-prefix kernels exist for this pool (16-bit K/V, blocks
+// of at least 16 tokens: the matrix-core tile).
+inline bool shared_prefix_supported(int32_t dtype, int32_t block_size) {
+  return dtype != kF32 && block_size >= 16;
+}
 
 // True when the decode kernels are instantiated for these sizes.
 bool decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);

@@ -90,3 +90,71 @@ def peak_key(case, seq, token, kv_head, group_rows, logit, head_dim, dtype, bloc
     table = case["tables"][seq]
     b = int(table[token // block_size])
     case["k_pool"][b, kv_head, token % block_size, :] = kf
+
+
+def build_families(families, kv_heads, group, head_dim, block_size, dtype, seed, scale=1.0, extra_blocks=4):
+    """Fork families written through the oracle into a NaN-poisoned pool.
+
+    ``families`` lists (prompt_len, [appended tokens per member]): member 0 is
+    the prompt's own sequence, the others fork from it before any append, and
+    each member then appends its tokens one at a time (copy-on-write copies
+    applied to the pool as the oracle block manager emits them).  The batch
+    is arranged by the oracle's dispatch order; returns the case dict of
+    ``build_case`` plus ``ids``, ``group_start``, ``prefix`` and
+    ``max_group``, the oracle's prefix groups of that batch."""
+    from oracle.kv_ops import copy_blocks as oracle_copy_blocks
+    rng = np.random.default_rng(seed)
+    bs = block_size
+    need = sum(-(-(p + max(app) + 1) // bs) * len(app) for p, app in families) + extra_blocks
+    order = rng.permutation(need)
+    bm = OracleBlockManager(need, bs, order)
+    bits_t = np.uint32 if dtype == "f32" else np.uint16
+    shape = (need, kv_heads, bs, head_dim)
+    k_pool = np.full(shape, NAN_BITS[dtype], dtype=bits_t)
+    v_pool = k_pool.copy()
+    ids = []
+    for f, (prompt, appends) in enumerate(families):
+        root = (f, 0)
+        bm.add_seq(root, prompt)
+        oracle_write_kv(k_pool, v_pool, draw(rng, (prompt, kv_heads, head_dim), dtype, scale),
+                        draw(rng, (prompt, kv_heads, head_dim), dtype, scale), bm.token_slots(root))
+        members = [root]
+        for c in range(1, len(appends)):
+            bm.fork(root, (f, c))
+            members.append((f, c))
+        for m, n in zip(members, appends):
+            for _ in range(n):
+                slot, src, dst = bm.append_slot(m)
+                if src >= 0:
+                    oracle_copy_blocks(k_pool, v_pool, [(src, dst)])
+                oracle_write_kv(k_pool, v_pool, draw(rng, (1, kv_heads, head_dim), dtype, scale),
+                                draw(rng, (1, kv_heads, head_dim), dtype, scale), [slot])
+        ids.extend(members)
+    ids = [ids[i] for i in bm.dispatch_order(ids)]
+    lens = np.array([bm.length(s) for s in ids], dtype=np.int32)
+    stride = max([-(-int(n) // bs) for n in lens] + [1])
+    tables = np.array(bm.padded_tables(ids, stride, pad=-1), dtype=np.int32)
+    q = draw(rng, (len(ids), kv_heads * group, head_dim), dtype, scale)
+    starts, prefix, largest = bm.prefix_groups(ids)
+    return dict(bm=bm, k_pool=k_pool, v_pool=v_pool, q=q, tables=tables, lens=lens, num_blocks=need, ids=ids,
+                group_start=np.array(starts, dtype=np.int32), prefix=np.array(prefix, dtype=np.int32),
+                max_group=largest)
+
+
+def run_shared_prefix(pk, case, kv_heads, head_dim, block_size, dtype, out_dtype=None, partition_tokens=0,
+                      group_start=None, prefix=None, max_prefix=None):
+    import torch
+    k = to_torch(case["k_pool"], dtype)
+    v = to_torch(case["v_pool"], dtype)
+    pool = pk.Pool(case["num_blocks"], block_size, kv_heads, head_dim, dtype, k=k, v=v)
+    gs = case["group_start"] if group_start is None else group_start
+    pre = case["prefix"] if prefix is None else prefix
+    max_len = int(max(case["lens"].max(), 0))
+    out = pk.decode_shared_prefix(
+        pool, to_torch(case["q"], dtype), torch.from_numpy(case["tables"]).cuda(),
+        torch.from_numpy(case["lens"]).cuda(), max_len, torch.from_numpy(np.asarray(gs, dtype=np.int32)).cuda(),
+        torch.from_numpy(np.asarray(pre, dtype=np.int32)).cuda(), case["max_group"],
+        int(pre.max()) if max_prefix is None else max_prefix, out_dtype=out_dtype,
+        partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out

@@ -56,6 +56,9 @@ def test_workload_scripts_agree(name):
     assert lens.tolist() == [ora.length(s) for s in sc.measured]
     assert lens.tolist() == [sc.lengths_before[s] + 1 for s in sc.measured]
     assert lib_bm.dispatch_order(sc.measured).tolist() == ora.dispatch_order(sc.measured)
+    ordered = [sc.measured[i] for i in ora.dispatch_order(sc.measured)]
+    starts, prefix, largest = lib_bm.prefix_groups(ordered)
+    assert (starts.tolist(), prefix.tolist(), largest) == ora.prefix_groups(ordered)
     assert_same_state(lib_bm, ora)
 
 
@@ -146,6 +149,8 @@ class ParityMachine(RuleBasedStateMachine):
         assert [tuple(p) for p in pairs.tolist()] == o_pairs
         assert lens.tolist() == [self.ora.length(s) for s in ids]
         assert self.lib.dispatch_order(ids).tolist() == self.ora.dispatch_order(ids)
+        starts, prefix, largest = self.lib.prefix_groups(ids)
+        assert (starts.tolist(), prefix.tolist(), largest) == self.ora.prefix_groups(ids)
 
     @precondition(lambda self: self.ora.seqs)
     @rule(data=st.data())

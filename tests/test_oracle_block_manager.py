@@ -340,3 +340,65 @@ def test_dispatch_order_properties(spec):
     assert maxima == sorted(maxima, reverse=True)
     for _, ns in runs:
         assert ns == sorted(ns, reverse=True)
+
+
+def test_prefix_groups_hand_example():
+    """P holds 40 tokens (blocks of 16: two full, one with 8); A and B fork
+    from P and A appends 3 tokens, which copies the shared third block.  The
+    run P, A, B shares two full blocks (32 tokens); X is alone (0)."""
+    bm = OracleBlockManager(64, 16)
+    bm.add_seq("P", 40)
+    bm.fork("P", "A")
+    bm.fork("P", "B")
+    for _ in range(3):
+        bm.append_slot("A")
+    bm.add_seq("X", 20)
+    assert bm.prefix_groups(["P", "A", "B", "X"]) == ([0, 3, 4], [32, 32, 32, 0], 3)
+    assert bm.prefix_groups(["X", "P", "A", "B"]) == ([0, 1, 4], [0, 32, 32, 32], 3)
+    # a sibling placed apart starts a run of its own
+    assert bm.prefix_groups(["P", "X", "A"]) == ([0, 1, 2, 3], [0, 0, 0], 1)
+    # B alone with P: the third block is shared but holds 8 tokens, so only two count
+    assert bm.prefix_groups(["P", "B"]) == ([0, 2], [32, 32], 2)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 70), st.integers(0, 3), st.integers(0, 40)), min_size=1, max_size=12),
+       st.randoms(use_true_random=False))
+def test_prefix_groups_properties(spec, rnd):
+    """Random fork families in a random batch order: runs are maximal and
+    contiguous, a prefix is whole blocks that every member holds, full and in
+    the same place, and it cannot grow by one more such block."""
+    bs = 4
+    bm = OracleBlockManager(8192, bs)
+    ids = []
+    for r, (n, k, g) in enumerate(spec):
+        bm.add_seq((r, 0), n)
+        ids.append((r, 0))
+        for c in range(1, k + 1):
+            bm.fork((r, 0), (r, c))
+            for _ in range((g * c) % 9):
+                bm.append_slot((r, c))
+            ids.append((r, c))
+    rnd.shuffle(ids)
+    starts, prefix, largest = bm.prefix_groups(ids)
+    assert starts[0] == 0 and starts[-1] == len(ids) and starts == sorted(set(starts))
+    assert largest == max(b - a for a, b in zip(starts, starts[1:]))
+    for a, b in zip(starts, starts[1:]):
+        members = ids[a:b]
+        tables = [bm.block_table(s)[0] for s in members]
+        firsts = [t[0] if t else None for t in tables]
+        assert all(f is not None and f == firsts[0] for f in firsts) or b - a == 1
+        if b < len(ids) and firsts[0] is not None:                       # maximal run
+            nxt = bm.block_table(ids[b])[0]
+            assert not nxt or nxt[0] != firsts[0]
+        p = prefix[a]
+        assert all(prefix[i] == p for i in range(a, b)) and p % bs == 0
+        if b - a == 1:
+            assert p == 0
+            continue
+        nb = p // bs
+        assert all(bm.length(s) >= p for s in members)
+        assert all(t[:nb] == tables[0][:nb] for t in tables)
+        grow_ok = (all(bm.length(s) >= p + bs for s in members) and
+                   all(len(t) > nb and t[nb] == tables[0][nb] for t in tables))
+        assert not grow_ok
