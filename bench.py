@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0 = the workload's setting (the library's automatic choice unless it names fixed "
                          "partitions); -1 = the balanced split; > 0 = fixed partitions of that many tokens")
+    ap.add_argument("--decode", choices=["auto", "plain", "shared"], default="auto",
+                    help="auto = pa_decode_shared_prefix when the batch has prefix groups, else pa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -103,30 +105,40 @@ def build_state(pk, w, sc, layers, steps_total):
     return dict(bm=bm, ids=ids, B=B, stride=stride, pools=pools, q=q, k_new=k_new, v_new=v_new, out=out)
 
 
+def meta_len(B, stride):
+    return B * (4 + stride) + 2 * B + 1
+
+
 class HostBuffers:
     """Pinned metadata written by the block manager, laid out as one int32 array
-    (slots | lens | copy pairs | block tables) so a step uploads it in one copy;
-    reused once that copy has left."""
+    (slots | lens | copy pairs | block tables | group starts | prefix tokens) so
+    a step uploads it in one copy; reused once that copy has left."""
 
     def __init__(self, B, stride):
         import torch
         self.B, self.stride = B, stride
-        self.flat = torch.empty(B * (4 + stride), dtype=torch.int32, pin_memory=True)
-        self.slots, self.lens, self.pairs, self.tables = split_meta(self.flat, B, stride)
+        self.flat = torch.empty(meta_len(B, stride), dtype=torch.int32, pin_memory=True)
+        self.slots, self.lens, self.pairs, self.tables, self.group_start, self.prefix = split_meta(self.flat, B, stride)
         self.lens_np = self.lens.numpy()
+        self.prefix_np = self.prefix.numpy()
         self.copied = None   # event recorded after the copy out of these buffers
 
 
 def split_meta(flat, B, stride):
-    """Views (slots[B], lens[B], pairs[B][2], tables[B][stride]) of one metadata array."""
-    return (flat[:B], flat[B:2 * B], flat[2 * B:4 * B].view(B, 2), flat[4 * B:].view(B, stride))
+    """Views (slots[B], lens[B], pairs[B][2], tables[B][stride], group_start[B+1],
+    prefix[B]) of one metadata array."""
+    t0 = 4 * B
+    t1 = t0 + B * stride
+    return (flat[:B], flat[B:2 * B], flat[2 * B:4 * B].view(B, 2), flat[t0:t1].view(B, stride),
+            flat[t1:t1 + B + 1], flat[t1 + B + 1:t1 + 2 * B + 1])
 
 
 # ----------------------------------------------------------------------------
 # the timed step
 # ----------------------------------------------------------------------------
-def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
-    """n_steps decode steps; returns per-step KV bytes read by decode."""
+def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, shared_prefix):
+    """n_steps decode steps; returns per-step KV bytes read by decode.  With
+    shared_prefix the batch's prefix groups go to pa_decode_shared_prefix."""
     import numpy as np
     import torch
     from paged_kv_cache_355_amd._lib import lib, check
@@ -149,6 +161,10 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
         n_cow = st["bm"].step_into(st["ids"].ctypes.data, B, hb.slots.data_ptr(), hb.pairs.data_ptr(),
                                    hb.tables.data_ptr(), stride, hb.lens.data_ptr())
         max_len = int(hb.lens_np.max())
+        if shared_prefix:
+            n_groups, max_group = st["bm"].prefix_groups_into(st["ids"].ctypes.data, B, hb.group_start.data_ptr(),
+                                                              hb.prefix.data_ptr())
+            max_prefix = int(hb.prefix_np.max())
         dev["flat"].copy_(hb.flat, non_blocking=True)
         if hb.copied is None:
             hb.copied = torch.cuda.Event()
@@ -163,10 +179,17 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing):
             if timing is not None:
                 ev0, ev1 = timing["free"].pop()
                 ev0.record(stream)
-            check(L.pa_decode(pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype],
-                              st["q"][layer].data_ptr(), B, w.q_heads, dev["tables"].data_ptr(), stride,
-                              dev["lens"].data_ptr(), max_len, 0.0, partition_tokens, ws.data_ptr(), ws_bytes,
-                              sptr), "pa_decode")
+            if shared_prefix:
+                check(L.pa_decode_shared_prefix(
+                    pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype], st["q"][layer].data_ptr(),
+                    B, w.q_heads, dev["tables"].data_ptr(), stride, dev["lens"].data_ptr(), max_len, 0.0, n_groups,
+                    dev["group_start"].data_ptr(), dev["prefix"].data_ptr(), max_group, max_prefix, partition_tokens,
+                    ws.data_ptr(), ws_bytes, sptr), "pa_decode_shared_prefix")
+            else:
+                check(L.pa_decode(pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype],
+                                  st["q"][layer].data_ptr(), B, w.q_heads, dev["tables"].data_ptr(), stride,
+                                  dev["lens"].data_ptr(), max_len, 0.0, partition_tokens, ws.data_ptr(), ws_bytes,
+                                  sptr), "pa_decode")
             if timing is not None:
                 ev1.record(stream)
                 timing["used"].append((ev0, ev1))
@@ -289,10 +312,10 @@ def kernel_source_hash():
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def recorded_traffic(workload):
+def recorded_traffic(workload, decode):
     """(HBM bytes per decode call, their ratio to the algorithmic bytes of the
     counted run) from the committed counter summary, if it was taken on the
-    current kernel source (else (None, None))."""
+    current kernel source with the same decode entry point (else (None, None))."""
     path = os.path.join(PROFILES, f"decode_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None, None
@@ -301,7 +324,7 @@ def recorded_traffic(workload):
         line = line.strip()
         if line.startswith("{"):
             rec = json.loads(line)
-    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("decode", "pa_decode") != decode:
         return None, None
     return rec.get("hbm_bytes_per_call"), round(rec["hbm_bytes_per_call"] / rec["algorithmic_bytes_per_call"], 4)
 
@@ -344,23 +367,36 @@ def main():
     B = st["B"]
     part = w.partition_tokens if args.partition_tokens == 0 else args.partition_tokens
     max_ctx_bound = st["stride"] * w.block_size
-    dev = {"flat": torch.empty(B * (4 + st["stride"]), dtype=torch.int32, device="cuda")}
-    dev["slots"], dev["lens"], dev["pairs"], dev["tables"] = split_meta(dev["flat"], B, st["stride"])
-    ws_bytes = pk.decode_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
+    dev = {"flat": torch.empty(meta_len(B, st["stride"]), dtype=torch.int32, device="cuda")}
+    (dev["slots"], dev["lens"], dev["pairs"], dev["tables"], dev["group_start"],
+     dev["prefix"]) = split_meta(dev["flat"], B, st["stride"])
+    # the sharing-aware decode when the batch has prefix groups (and it was not turned off)
+    _, probe_prefix, _ = st["bm"].prefix_groups(st["ids"][st["bm"].dispatch_order(st["ids"])])
+    shared_prefix = args.decode == "shared" or (args.decode == "auto" and int(probe_prefix.max(initial=0)) > 0)
+    if shared_prefix and part < 0:
+        part = 0
+    if shared_prefix:
+        ws_bytes = pk.decode_shared_prefix_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound,
+                                                           max_ctx_bound, part)
+        resolved_part = part if part > 0 else (
+            -(-max_ctx_bound // w.block_size) * w.block_size
+            if pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, 0) > 0 else 512)
+    else:
+        ws_bytes = pk.decode_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
+        resolved_part = pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
     dev["workspace"] = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")   # counters start at 0
-    resolved_part = pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
     hbufs = [HostBuffers(B, st["stride"]) for _ in range(2)]
     torch.cuda.synchronize()
     log(f"[bench] state ready; warmup {args.warmup} steps")
 
-    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None)
+    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None, shared_prefix)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     timing = {"used": [], "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                                    for _ in range(args.steps * args.layers)]}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    kv_bytes = run_steps(pk, w, st, args.steps, part, dev, hbufs, args.warmup, timing)
+    kv_bytes = run_steps(pk, w, st, args.steps, part, dev, hbufs, args.warmup, timing, shared_prefix)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     dec_ms = [a.elapsed_time(b) for a, b in timing["used"]]
@@ -373,7 +409,7 @@ def main():
     achieved = per_call_bytes / mean_dec_s / 1e9
     value = total_kv / elapsed / 1e9
     layers = len(st["pools"])
-    traffic, traffic_ratio = recorded_traffic(w.name)
+    traffic, traffic_ratio = recorded_traffic(w.name, "pa_decode_shared_prefix" if shared_prefix else "pa_decode")
     dec_sorted = sorted(dec_ms)
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seq-steps/s, 7B shape",
@@ -392,6 +428,7 @@ def main():
             "workload": w.name, "batch": B, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "pool_blocks": sc.num_blocks,
             "layers_per_step": layers, "partition_tokens": resolved_part,
+            "decode": "pa_decode_shared_prefix" if shared_prefix else "pa_decode",
             "context_lens": "uniform [128, 2048] before the first warmup step, +1 per step"
             if w.name == "mha7b_fp16" else w.notes,
             "mean_context_len_timed": round(total_kv / (args.steps * layers * 2 * w.kv_heads * w.head_dim *
@@ -406,7 +443,9 @@ def main():
                            "p50": round(dec_sorted[len(dec_sorted) // 2] * 1e3, 2),
                            "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2)},
         "roofline": {
-            "kernel": ("pa_decode: decode_balanced_kernel" if resolved_part < 0 else
+            "kernel": ("pa_decode_shared_prefix: decode_prefix_kernel + decode_partition_kernel + "
+                       "decode_reduce_kernel" if shared_prefix else
+                       "pa_decode: decode_balanced_kernel" if resolved_part < 0 else
                        "pa_decode: decode_partition_kernel" + (" + decode_reduce_kernel"
                                                                if resolved_part < max_ctx_bound else
                                                                " (one workgroup per sequence and kv-head)")),

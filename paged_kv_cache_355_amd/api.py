@@ -298,6 +298,14 @@ class BlockManager:
                                         ctypes.addressof(ng), ctypes.addressof(mg)), "pa_bm_prefix_groups")
         return starts[:ng.value + 1].copy(), prefix[:n].copy(), mg.value
 
+    def prefix_groups_into(self, ids_ptr, n, starts_ptr, prefix_ptr):
+        """``prefix_groups`` writing straight into caller buffers (e.g. pinned
+        tensors of n + 1 and n int32); returns (num_groups, max_group_size)."""
+        ng, mg = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().pa_bm_prefix_groups(self.handle, ids_ptr, n, starts_ptr, prefix_ptr, ctypes.addressof(ng),
+                                        ctypes.addressof(mg)), "pa_bm_prefix_groups")
+        return ng.value, mg.value
+
     def refcount(self, block):
         rc = ctypes.c_int32()
         check(lib().pa_bm_refcount(self.handle, int(block), ctypes.addressof(rc)), "pa_bm_refcount")

@@ -46,6 +46,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <type_traits>
@@ -807,6 +808,21 @@ __device__ __forceinline__ int32_t parts_of(int32_t n, int32_t part_tokens) {
   return n <= 0 ? 0 : (n + part_tokens - 1) / part_tokens;
 }
 
+// Fold n partial records (rows prow0 … prow0 + n − 1) of output element d into
+// the running (M, L, O): the online-softmax merge by running max and sum.
+template <int D>
+__device__ __forceinline__ void fold_parts(const float* __restrict__ part_ml, const float* __restrict__ part_o,
+                                           int64_t prow0, int32_t n, int d, float& M, float& L, float& O) {
+  for (int32_t i = 0; i < n; ++i) {
+    const float m_i = part_ml[2 * (prow0 + i)];
+    const float mt = fmaxf(M, m_i);
+    const float a = exp2f_fast(M - mt), b = exp2f_fast(m_i - mt);
+    L = L * a + part_ml[2 * (prow0 + i) + 1] * b;
+    O = O * a + part_o[(prow0 + i) * D + d] * b;
+    M = mt;
+  }
+}
+
 // Write zero rows (an empty context) or NaN rows (an invalid length) for all
 // query heads of kv-head range [g0, g1) of sequence s.
 template <int D, int G>
@@ -867,12 +883,23 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
     return;
   }
   // With a shared prefix this workgroup covers part p of the suffix; the
-  // prefix's npp partials come from decode_prefix_kernel.
+  // prefix's npp partials were written by decode_prefix_kernel, which ran
+  // before this kernel on the stream.  A suffix of one part folds them in
+  // here; longer ones leave it to decode_reduce_kernel.
   const int32_t pre = prefix_of<BS>(seq_prefix, s, len_c, max_prefix);
   const int32_t npp = parts_of(pre, part_tokens);
   const int32_t nsp = parts_of(len_c - pre, part_tokens);
-  if (p >= nsp) return;
-  const int32_t nparts = npp + nsp;
+  if (p >= max(nsp, 1)) return;
+  if (nsp == 0) {   // the context is all prefix: finish from its partials
+    for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+      const int r = idx / D, d = idx - r * D;
+      const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
+      float M = kNegBig, L = 0.f, O = 0.f;
+      fold_parts<D>(part_ml, part_o, row * max_parts, npp, d, M, L, O);
+      store_out(out, out_dtype, row * D + d, L > 0.f ? O / L : (L != L ? qnan() : 0.f));
+    }
+    return;
+  }
   const int32_t t_begin = pre + p * part_tokens;
   const int32_t t_end = min(t_begin + part_tokens, len_c);
   const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
@@ -883,8 +910,9 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
       shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
-        if (nparts == 1) {
-          store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
+        if (nsp == 1) {
+          if (npp > 0) fold_parts<D>(part_ml, part_o, row * max_parts, npp, d, M, L, O);
+          store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : (L != L ? qnan() : 0.f)));
         } else {
           const int64_t prow = row * max_parts + npp + p;
           part_o[prow * D + d] = bad ? qnan() : O;
@@ -968,7 +996,8 @@ __global__ __launch_bounds__(NW * 64) void decode_prefix_kernel(
 // decode_reduce_kernel: merge the partitions of sequences longer than one.
 //   grid = (q_heads, num_seqs, D/DC), block = kReduceThreads; one workgroup
 //   per DC output dims of a row.  With a shared prefix a row's parts are the
-//   prefix's partials followed by the suffix's.
+//   prefix's partials followed by the suffix's; rows whose suffix is one
+//   part were finished by the partition kernel.
 //   out = Σ_p 2^(m_p − M) o_p / Σ_p 2^(m_p − M) l_p with M = max_p m_p.
 //   Each workgroup computes the per-partition weights 2^(m_p − M) into LDS
 //   (up to kReduceLds partitions; beyond that they are recomputed on the
@@ -1024,8 +1053,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
   const int32_t pre = prefix_of<BS>(seq_prefix, s, len_c, max_prefix);
-  const int32_t nparts = parts_of(pre, part_tokens) + parts_of(len_c - pre, part_tokens);
-  if (len_c == 0 || (pre == 0 && nparts == 1)) return;  // written by the partition kernel (NaN rows included)
+  const int32_t nsp = parts_of(len_c - pre, part_tokens);
+  if (nsp <= 1) return;  // finished by the partition kernel (empty, NaN and single-part rows)
+  const int32_t nparts = parts_of(pre, part_tokens) + nsp;
   const int64_t row = static_cast<int64_t>(s) * q_heads + h;
   const float* ml = part_ml + row * max_parts * 2;
   const float* po = part_o + row * max_parts * D;
@@ -1446,16 +1476,18 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
     }
   }
   const int32_t* seq_prefix = shared_prefix ? a.seq_prefix : nullptr;
-  // suffix partitions: at most max_parts minus the prefix's (the host sizes
-  // max_parts as prefix parts + context parts, so this covers every suffix)
-  dim3 grid(a.max_parts, p.kv_heads, a.num_seqs);
+  // partitions of the longest suffix (the whole context without a prefix)
+  const int32_t suffix_parts =
+      static_cast<int32_t>(std::max<int64_t>(1, (static_cast<int64_t>(a.max_context_len) + a.partition_tokens - 1) /
+                                                    a.partition_tokens));
+  dim3 grid(suffix_parts, p.kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
                      a.table_stride, a.context_lens, seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads,
                      a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
+  if (e != hipSuccess || suffix_parts <= 1) return e;
   // fewer rows than CUs: split each row's dims over D/16 workgroups
   if (static_cast<int64_t>(a.q_heads) * a.num_seqs < kReduceSplitRows) {
     hipLaunchKernelGGL((decode_reduce_kernel<D, 16, BS>), dim3(a.q_heads, a.num_seqs, D / 16), dim3(kReduceThreads),

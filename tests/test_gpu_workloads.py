@@ -70,9 +70,11 @@ def _sample(ids, lens, k, seed):
     return sorted(picks)
 
 
-def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None):
+def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None, shared_prefix=False):
     """One decode step of workload ``name`` on the GPU, checked against the
-    oracle (``partition_tokens`` overrides the workload's split)."""
+    oracle (``partition_tokens`` overrides the workload's split).  With
+    ``shared_prefix`` the batch is arranged in the oracle's dispatch order and
+    decoded by pa_decode_shared_prefix with the oracle's prefix groups."""
     import torch
     w = WORKLOADS[name]
     sc = make_scenario(w)
@@ -84,6 +86,8 @@ def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None):
     else:
         _apply(ora, sc.all_ops())
         ids = sc.measured
+    if shared_prefix:
+        ids = [ids[i] for i in ora.dispatch_order(ids)]
     print(f"[{name}{' cow' if cow_step else ''}] {len(ids)} seqs, pool {sc.num_blocks} blocks", flush=True)
 
     pool = pk.Pool(sc.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype)
@@ -105,8 +109,17 @@ def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None):
     if pairs:
         pk.copy_blocks(pool, torch.tensor(pairs, dtype=torch.int32, device="cuda"))
     pk.write_kv(pool, k_new, v_new, torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda())
-    out = pk.decode(pool, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), max_len,
-                    partition_tokens=w.partition_tokens if partition_tokens is None else partition_tokens)
+    part = w.partition_tokens if partition_tokens is None else partition_tokens
+    if shared_prefix:
+        starts, prefix, largest = ora.prefix_groups(ids)
+        assert max(prefix) > 0
+        out = pk.decode_shared_prefix(pool, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                      max_len, torch.tensor(starts, dtype=torch.int32, device="cuda"),
+                                      torch.tensor(prefix, dtype=torch.int32, device="cuda"), largest, max(prefix),
+                                      partition_tokens=part)
+    else:
+        out = pk.decode(pool, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), max_len,
+                        partition_tokens=part)
     torch.cuda.synchronize()
 
     # pool bytes after the step: oracle copy + write on the host copy of the start state
@@ -190,6 +203,15 @@ def test_prefix_share_cow_step_full(gpu):
 def test_prefix_share_steady_full(gpu):
     r = run_step(gpu, "prefix_share_fp16")
     assert r["pairs"] == []
+
+
+@pytest.mark.parametrize("cow_step", [False, True])
+def test_prefix_share_shared_prefix_decode_full(gpu, cow_step):
+    """The prefix-sharing batch (32 prompts x 8 samples) through the
+    sharing-aware decode: each prompt's 1024-token prefix read once per
+    kv-head, checked on sampled sequences against the oracle."""
+    r = run_step(gpu, "prefix_share_fp16", cow_step=cow_step, samples=10, shared_prefix=True)
+    assert len(r["pairs"]) == (224 if cow_step else 0)
 
 
 def test_long_splitk_bf16_full(gpu):
