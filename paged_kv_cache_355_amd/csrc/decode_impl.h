@@ -218,17 +218,22 @@ constexpr int kMinWavesPerEU = kUseMfma<DT, BS, G> ? (BALANCED ? 1 : 3) : (G <= 
 
 template <int NW, int G, int D, bool MFMA>
 struct WaveMerge {
-  float o[NW][G][D];
+  // matrix-core path: each wave's V tile, 16 tokens × D.  Lane quarter qd
+  // reads rows 4qd..4qd+3; a row of D/2 + 2 dwords puts the quarters 8 banks
+  // apart (4·(D/2 + 2) ≡ 8 mod 32), so one transposed read touches 32
+  // distinct banks.  kt is the K tile, read back in the A layout.
+  struct Tiles {
+    uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
+    uint16_t kt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
+  };
+  union {             // the tiles live during the token loop, o after it
+    float o[NW][G][D];
+    Tiles t;
+  };
   float m[NW][G];
   float l[NW][G];
   int bad[NW];
   int32_t tbl[kTableBatch];   // physical block ids, -1 for an id outside the pool
-  // matrix-core path: each wave's V tile, 16 tokens × D.  Lane quarter qd
-  // reads rows 4qd..4qd+3; a row of D/2 + 2 dwords puts the quarters 8 banks
-  // apart (4·(D/2 + 2) ≡ 8 mod 32), so one transposed read touches 32
-  // distinct banks.
-  uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
-  uint16_t kt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];   // K tile, read back in the A layout
 };
 
 // A 16-byte K/V load.  STREAM selects the non-temporal (streaming) cache
@@ -407,7 +412,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
         const int row = i * RPI + vrow;
-        uint2* dst = reinterpret_cast<uint2*>(&sh.kt[wave][row][(lane % LPR) * 8]);
+        uint2* dst = reinterpret_cast<uint2*>(&sh.t.kt[wave][row][(lane % LPR) * 8]);
         dst[0] = make_uint2(kb[i].x, kb[i].y);
         dst[1] = make_uint2(kb[i].z, kb[i].w);
       }
@@ -416,7 +421,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       uint4 ka_op[NKL];
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        const uint2* src = reinterpret_cast<const uint2*>(&sh.kt[wave][tl][32 * i + 8 * qd]);
+        const uint2* src = reinterpret_cast<const uint2*>(&sh.t.kt[wave][tl][32 * i + 8 * qd]);
         const uint2 lo = src[0], hi = src[1];
         ka_op[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
@@ -430,7 +435,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       for (int i = 0; i < NKL; ++i) {
         const int row = i * RPI + vrow;
         const uint4 v = tok0 + row < te ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
-        uint2* dst = reinterpret_cast<uint2*>(&sh.vt[wave][row][(lane % LPR) * 8]);   // rows are 8-byte aligned
+        uint2* dst = reinterpret_cast<uint2*>(&sh.t.vt[wave][row][(lane % LPR) * 8]);   // rows are 8-byte aligned
         dst[0] = make_uint2(v.x, v.y);
         dst[1] = make_uint2(v.z, v.w);
       }
@@ -474,10 +479,10 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       // Oᵀ += Vᵀ·Pᵀ: lane reads dim 16b + tl of tokens 4qd..4qd+3
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const uint32_t v0 = sh.vt[wave][4 * qd + 0][16 * b + tl];
-        const uint32_t v1 = sh.vt[wave][4 * qd + 1][16 * b + tl];
-        const uint32_t v2 = sh.vt[wave][4 * qd + 2][16 * b + tl];
-        const uint32_t v3 = sh.vt[wave][4 * qd + 3][16 * b + tl];
+        const uint32_t v0 = sh.t.vt[wave][4 * qd + 0][16 * b + tl];
+        const uint32_t v1 = sh.t.vt[wave][4 * qd + 1][16 * b + tl];
+        const uint32_t v2 = sh.t.vt[wave][4 * qd + 2][16 * b + tl];
+        const uint32_t v3 = sh.t.vt[wave][4 * qd + 3][16 * b + tl];
         const uint2 a = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
         ob[b] = mfma_k16<DT>(a, phi, ob[b]);
         ob[b] = mfma_k16<DT>(a, plo, ob[b]);
@@ -504,7 +509,9 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
 
-  // Merge the NW waves through LDS and hand each output to emit.
+  // Merge the NW waves through LDS and hand each output to emit.  o shares
+  // its LDS with the tiles, so every wave must be done with them first.
+  __syncthreads();
   if (tl < R) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -942,7 +949,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
 //   held in one tile streams its prefix.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_prefix_kernel(
+__global__ __launch_bounds__(NW * 64, 3) void decode_prefix_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     float* __restrict__ part_ml, float* __restrict__ part_o, const int32_t* __restrict__ block_tables,
     int32_t table_stride, const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
