@@ -443,8 +443,8 @@ def main():
                            "p50": round(dec_sorted[len(dec_sorted) // 2] * 1e3, 2),
                            "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2)},
         "roofline": {
-            "kernel": ("pa_decode_shared_prefix: decode_prefix_kernel + decode_partition_kernel + "
-                       "decode_reduce_kernel" if shared_prefix else
+            "kernel": ("pa_decode_shared_prefix: decode_prefix_kernel + decode_partition_kernel" +
+                       (" + decode_reduce_kernel" if resolved_part < max_ctx_bound else "") if shared_prefix else
                        "pa_decode: decode_balanced_kernel" if resolved_part < 0 else
                        "pa_decode: decode_partition_kernel" + (" + decode_reduce_kernel"
                                                                if resolved_part < max_ctx_bound else
