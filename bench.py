@@ -59,6 +59,8 @@ def parse_args():
     ap.add_argument("--decode", choices=["auto", "plain", "shared"], default="auto",
                     help="auto = pa_decode_shared_prefix when the batch has prefix groups, else pa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-admission (bulk pa_write_kv) probe")
+    ap.add_argument("--no-swap", action="store_true", help="skip the block swap (pa_swap_out / pa_swap_in) probe")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run a plain elementwise copy of this many MiB three times "
@@ -329,6 +331,91 @@ def recorded_traffic(workload, decode):
     return rec.get("hbm_bytes_per_call"), round(rec["hbm_bytes_per_call"] / rec["algorithmic_bytes_per_call"], 4)
 
 
+def prefill_probe(pk, w, st, reps=5):
+    """Prompt admission at prompt scale: a fresh block manager over the first
+    layer's pool admits a second seeded draw of the workload's prompts
+    (add_seq, then each prompt's token slots), and one bulk pa_write_kv writes
+    every prompt token's K and V (partial last blocks included).  Runs after
+    the timed decode steps, whose pool contents it overwrites."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_355_amd._lib import lib, check
+    from workloads import make_scenario, device_fill_, seed_for
+
+    pool = st["pools"][0]
+    sc2 = make_scenario(w, repetition=1)
+    prompts = [(op[1], op[2]) for op in sc2.setup if op[0] == "add"]
+    seed = seed_for(w, 1)
+    bm = pk.BlockManager(pool.num_blocks, w.block_size, np.random.default_rng(seed).permutation(pool.num_blocks))
+    t0 = time.perf_counter()
+    slots = []
+    admitted = 0
+    for sid, n in prompts:
+        try:
+            bm.add_seq(sid, n)
+        except pk.NoBlocksError:
+            break
+        slots.append(bm.token_slots(sid, 0, n))
+        admitted += 1
+    slots = np.concatenate(slots).astype(np.int32)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    n_tok = int(slots.shape[0])
+    tdt = pk.torch_dtype(w.dtype)
+    k_new = device_fill_(torch.empty((n_tok, w.kv_heads, w.head_dim), dtype=tdt, device="cuda"), seed + 11,
+                         w.value_scale)
+    v_new = device_fill_(torch.empty_like(k_new), seed + 12, w.value_scale)
+    slots_dev = torch.from_numpy(slots).cuda()
+    stream = torch.cuda.current_stream()
+    L = lib()
+    args = (pool.handle, k_new.data_ptr(), v_new.data_ptr(), slots_dev.data_ptr(), n_tok, stream.cuda_stream)
+    check(L.pa_write_kv(*args), "pa_write_kv")   # warm-up (re-writing the same slots is idempotent)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        check(L.pa_write_kv(*args), "pa_write_kv")
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    moved = 2 * 2 * n_tok * w.kv_heads * w.head_dim * pk.api.ELEM_BYTES[w.dtype]   # K and V, read + write
+    del k_new, v_new, slots_dev
+    return {"prompts": admitted, "tokens": n_tok, "host_admit_ms": round(host_ms, 3),
+            "write_kv_us": round(us, 2), "write_kv_GBps": round(moved / us / 1e3, 1),
+            "frac_of_hbm_peak": round(moved / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "bytes": "K and V of every prompt token, read from the staging tensors and written into the pool"}
+
+
+def swap_probe(pk, st, target_mib=256, reps=3):
+    """Block swap between the first layer's pool and pinned host memory: about
+    target_mib MiB of whole blocks out (pa_swap_out) and back into the same
+    blocks (pa_swap_in, which restores the bytes it just saved)."""
+    import torch
+    from paged_kv_cache_355_amd._lib import lib, check
+
+    pool = st["pools"][0]
+    per_block = 2 * pool.block_bytes
+    n = max(1, min(pool.num_blocks, (target_mib << 20) // per_block))
+    blocks = torch.arange(n, dtype=torch.int32, device="cuda")
+    host = torch.empty(n * per_block, dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    L = lib()
+    res = {}
+    for name, fn in (("out", L.pa_swap_out), ("in", L.pa_swap_in)):
+        args = (pool.handle, blocks.data_ptr(), n, host.data_ptr(), n * per_block, stream.cuda_stream)
+        check(fn(*args), f"pa_swap_{name}")   # warm-up
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            check(fn(*args), f"pa_swap_{name}")
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+        res[f"swap_{name}_us"] = round(us, 1)
+        res[f"swap_{name}_GBps"] = round(n * per_block / us / 1e3, 2)
+    res.update({"blocks": n, "bytes": n * per_block,
+                "path": "one kernel between HBM and pinned host memory, no staging copy"})
+    return res
+
+
 def copy_probe(mib):
     """A plain elementwise kernel of known traffic (reads and writes mib MiB)."""
     import torch
@@ -461,6 +548,10 @@ def main():
         "cpu_baseline": None,
     }
     result["memory"] = memory_accounting(st["bm"], w)
+    if not args.no_prefill:
+        result["prefill"] = prefill_probe(pk, w, st)
+    if not args.no_swap:
+        result["swap"] = swap_probe(pk, st)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:

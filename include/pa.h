@@ -152,6 +152,26 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
                                      int32_t max_context_len, int32_t partition_tokens,
                                      int32_t* resolved);
 
+/* Block swap between the pool and pinned host memory ([P2] §5, §8: blocks
+ * of an inactive sequence move to CPU memory and back, as pages are swapped).
+ *   blocks: device int32[n], pool block ids; ids outside the pool are skipped.
+ *   host: pinned host memory the device can map (hipHostMalloc, or a torch
+ *     tensor made with pin_memory=True), 16-byte aligned, host_bytes ≥
+ *     n × 2 × block_bytes.  Layout [n][2][block_bytes]: block i's K tile (all
+ *     kv-heads) then its V tile, each in the pool's [kv_heads][block_size]
+ *     [head_dim] order.
+ *   pa_swap_out copies pool → host, pa_swap_in host → pool (blocks distinct).
+ *   One kernel moves the bytes straight between HBM and host memory over the
+ *   host link: no staging buffer, no allocation.  Asynchronous on stream: the
+ *   host reads swapped-out bytes after synchronising the stream, and keeps the
+ *   buffer unchanged until a swap-in has completed.
+ * Errors: PA_ERR_INVALID (bad pointer or size; host memory that is not
+ * pinned and mapped), PA_ERR_HIP. */
+pa_status pa_swap_out(const pa_pool* pool, const int32_t* blocks, int32_t n, void* host, int64_t host_bytes,
+                      void* stream);
+pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void* host, int64_t host_bytes,
+                     void* stream);
+
 /* out[s][h] = softmax(q[s][h] · K_sᵀ · scale) · V_s over the context_lens[s]
  * tokens of sequence s, whose token t lives at slot
  * block_tables[s*block_table_stride + t/block_size]*block_size + t%block_size.
@@ -265,6 +285,9 @@ typedef struct pa_bm_stats_t {
   int64_t logical_blocks;  /* sum of block-table lengths                     */
   int64_t filled_slots;    /* slots of used blocks holding a token (unique)  */
   int64_t cow_copies;      /* copy-on-write pairs emitted so far             */
+  int32_t swapped_seqs;    /* sequences swapped out (not in num_seqs)        */
+  int32_t reserved;        /* 0                                              */
+  int64_t swapped_tokens;  /* sum of their lengths                           */
 } pa_bm_stats_t;
 
 pa_status pa_bm_create(int32_t num_blocks, int32_t block_size,
@@ -344,6 +367,26 @@ pa_status pa_bm_dispatch_order(const pa_bm* bm, const int64_t* seq_ids, int32_t 
  * Errors: PA_ERR_INVALID, PA_ERR_NOT_FOUND. */
 pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* group_start,
                               int32_t* prefix_tokens, int32_t* num_groups, int32_t* max_group_size);
+
+/* Swap a sequence out ([P2] §5, §8: inactive blocks move to CPU memory, as
+ * pages are swapped).  blocks (host int32, cap entries) receives its block
+ * table in order — the source blocks for pa_swap_out — and *n_blocks its
+ * length; each block's refcount then drops (blocks reaching 0 join the free
+ * list in table order) and the sequence keeps only its length.  Until
+ * pa_bm_swap_in every other call treats it as unknown, except pa_bm_free_seq.
+ * The blocks may be handed out again at once: enqueue pa_swap_out on the
+ * stream before any write that could reuse them.
+ * Errors: PA_ERR_NOT_FOUND, PA_ERR_INVALID (cap too small; *n_blocks is set,
+ * nothing changes). */
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap, int32_t* n_blocks);
+
+/* Swap a sequence back in: it takes ⌈length / block_size⌉ blocks from the
+ * free list (its new table, every block private with refcount 1; blocks it
+ * shared before swap-out are not shared again), returned in table order in
+ * blocks — the destinations for pa_swap_in.
+ * Errors: PA_ERR_NOT_FOUND (not swapped out), PA_ERR_NO_BLOCKS (no change),
+ * PA_ERR_INVALID (cap too small; *n_blocks is set, nothing changes). */
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap, int32_t* n_blocks);
 
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc);
 

@@ -40,6 +40,14 @@ implementations agree bit for bit):
 5. ``free_seq`` decrements refcounts in table order; blocks reaching zero join
    the tail of the free list in that order.
 
+Swapping ([P2 §5], [P2 §8]: inactive blocks go to CPU memory and come back,
+as pages are swapped): ``swap_out`` hands back a sequence's table (the blocks
+whose bytes go to the host) and releases those blocks as ``free_seq`` would;
+the sequence keeps only its length.  ``swap_in`` takes ⌈length/bs⌉ fresh
+blocks, all private, as its new table (the destinations of the copy back).
+Readings: blocks shared before swap-out are not shared again after swap-in;
+a swapped sequence is unknown to every other call except ``free_seq``.
+
 ``dispatch_order`` is not from the pages: it is the library's scheduling
 choice for a decode batch (longest processing time first over groups of
 sequences that share their first physical block), stated here so that the
@@ -72,6 +80,7 @@ class OracleBlockManager:
         self.free = deque(order)
         self.rc = [0] * num_blocks
         self.seqs = {}
+        self.swapped = {}   # seq id -> length while swapped out
         self.cow_copies = 0
 
     # -- allocation primitives -------------------------------------------------
@@ -87,7 +96,7 @@ class OracleBlockManager:
     # -- sequence lifecycle ----------------------------------------------------
     def add_seq(self, seq_id, num_tokens):
         """Prefill allocation: ⌈n/bs⌉ fresh blocks, each with refcount 1."""
-        if seq_id in self.seqs:
+        if seq_id in self.seqs or seq_id in self.swapped:
             raise KeyError(f"sequence {seq_id} already exists")
         if num_tokens < 0:
             raise ValueError("num_tokens must be >= 0")
@@ -101,7 +110,7 @@ class OracleBlockManager:
         """The child shares every block of the parent; each refcount rises by one."""
         if parent_id not in self.seqs:
             raise KeyError(f"unknown parent {parent_id}")
-        if child_id in self.seqs:
+        if child_id in self.seqs or child_id in self.swapped:
             raise KeyError(f"sequence {child_id} already exists")
         parent = self.seqs[parent_id]
         for b in parent.table:
@@ -172,8 +181,30 @@ class OracleBlockManager:
                 pairs.append((src, dst))
         return slots, pairs
 
+    def swap_out(self, seq_id):
+        """The sequence's blocks in table order; they are released as by free_seq
+        and the sequence keeps only its length."""
+        seq = self.seqs[seq_id]
+        blocks = list(seq.table)
+        self.free_seq(seq_id)
+        self.swapped[seq_id] = seq.length
+        return blocks
+
+    def swap_in(self, seq_id):
+        """⌈length/bs⌉ fresh private blocks as the sequence's new table."""
+        length = self.swapped[seq_id]
+        need = self._blocks_for(length)
+        if need > len(self.free):
+            raise NoBlocksError(f"swap-in needs {need} blocks, {len(self.free)} free")
+        del self.swapped[seq_id]
+        self.seqs[seq_id] = _Seq([self._pop_free() for _ in range(need)], length)
+        return list(self.seqs[seq_id].table)
+
     def free_seq(self, seq_id):
         """Release: refcount -1 per block in table order; zeros rejoin the free tail."""
+        if seq_id in self.swapped:
+            del self.swapped[seq_id]
+            return
         seq = self.seqs.pop(seq_id)
         for b in seq.table:
             self.rc[b] -= 1
@@ -280,4 +311,6 @@ class OracleBlockManager:
             "logical_blocks": sum(len(s.table) for s in self.seqs.values()),
             "filled_slots": sum(fill.values()),
             "cow_copies": self.cow_copies,
+            "swapped_seqs": len(self.swapped),
+            "swapped_tokens": sum(self.swapped.values()),
         }

@@ -10,6 +10,9 @@ round-trip.
   the slot its block table assigns.  Slot ``s`` is (block ⌊s/bs⌋, offset
   s mod bs) ([P2 §5]); a slot of -1 means "skip this row" (padding in a
   batch).
+* ``swap_out`` / ``swap_in`` — whole blocks to and from a host array shaped
+  ``[n][2][kv_heads][block_size][head_dim]`` (block i's K tile, then its V
+  tile), the byte moves of swapping ([P2 §5], [P2 §8]).
 * ``copy_blocks`` — the copy half of copy-on-write ([P2 §3.4]): the whole
   block (every kv-head, every slot, K and V) is duplicated from src to dst.
   The pairs of one call act as if simultaneous; a call whose destinations
@@ -61,3 +64,26 @@ def copy_blocks(k_pool, v_pool, pairs):
     v_src = v_pool[srcs].copy()
     k_pool[dsts] = k_src
     v_pool[dsts] = v_src
+
+
+def swap_out(k_pool, v_pool, blocks):
+    """Host copy of whole blocks: out[i][0] = K tile of blocks[i], out[i][1] = its V tile."""
+    blocks = [int(b) for b in blocks]
+    for b in blocks:
+        if not 0 <= b < k_pool.shape[0]:
+            raise IndexError(f"block {b} outside the pool")
+    return np.stack([k_pool[blocks], v_pool[blocks]], axis=1) if blocks else \
+        np.empty((0, 2) + k_pool.shape[1:], dtype=k_pool.dtype)
+
+
+def swap_in(k_pool, v_pool, blocks, host):
+    """Write host[i][0] / host[i][1] into the K / V tile of blocks[i] (distinct blocks)."""
+    blocks = [int(b) for b in blocks]
+    if len(set(blocks)) != len(blocks):
+        raise ValueError("a block is swapped in twice")
+    for b in blocks:
+        if not 0 <= b < k_pool.shape[0]:
+            raise IndexError(f"block {b} outside the pool")
+    for i, b in enumerate(blocks):
+        k_pool[b] = host[i, 0]
+        v_pool[b] = host[i, 1]

@@ -31,7 +31,8 @@ class BmStats(ctypes.Structure):
     _fields_ = [
         ("num_blocks", c_i32), ("block_size", c_i32), ("free_blocks", c_i32), ("used_blocks", c_i32),
         ("shared_blocks", c_i32), ("num_seqs", c_i32), ("logical_tokens", c_i64), ("logical_blocks", c_i64),
-        ("filled_slots", c_i64), ("cow_copies", c_i64),
+        ("filled_slots", c_i64), ("cow_copies", c_i64), ("swapped_seqs", c_i32), ("reserved", c_i32),
+        ("swapped_tokens", c_i64),
     ]
 
 
@@ -45,6 +46,8 @@ SIGNATURES = {
     "pa_pool_info": (c_i32, [c_p, c_p, c_p, c_p]),
     "pa_write_kv": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_p]),
     "pa_copy_blocks": (c_i32, [c_p, c_p, c_i32, c_p]),
+    "pa_swap_out": (c_i32, [c_p, c_p, c_i32, c_p, c_i64, c_p]),
+    "pa_swap_in": (c_i32, [c_p, c_p, c_i32, c_p, c_i64, c_p]),
     "pa_decode_workspace_bytes": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_p]),
     "pa_decode_partition_tokens": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_p]),
     "pa_decode": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_i32, c_p, c_i32, c_p, c_i32, ctypes.c_float, c_i32,
@@ -64,6 +67,8 @@ SIGNATURES = {
     "pa_bm_tables": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_p]),
     "pa_bm_dispatch_order": (c_i32, [c_p, c_p, c_i32, c_p]),
     "pa_bm_prefix_groups": (c_i32, [c_p, c_p, c_i32, c_p, c_p, c_p, c_p]),
+    "pa_bm_swap_out": (c_i32, [c_p, c_i64, c_p, c_i32, c_p]),
+    "pa_bm_swap_in": (c_i32, [c_p, c_i64, c_p, c_i32, c_p]),
     "pa_bm_refcount": (c_i32, [c_p, c_i32, c_p]),
     "pa_bm_free_list": (c_i32, [c_p, c_p, c_i32, c_p]),
     "pa_bm_stats": (c_i32, [c_p, c_p]),

@@ -102,6 +102,30 @@ def copy_blocks(pool, pairs, stream=None):
           "pa_copy_blocks")
 
 
+def _swap(pool, blocks, host, out, stream):
+    import torch
+    n = int(blocks.shape[0])
+    if n == 0:
+        return
+    if host.device.type != "cpu" or not host.is_pinned() or not host.is_contiguous():
+        raise ValueError("host must be a contiguous pinned CPU tensor (pin_memory=True)")
+    nbytes = host.numel() * host.element_size()
+    fn = lib().pa_swap_out if out else lib().pa_swap_in
+    check(fn(pool.handle, _dev_ptr(blocks, "blocks", torch.int32, (n,)), n, host.data_ptr(), nbytes, _stream(stream)),
+          "pa_swap_out" if out else "pa_swap_in")
+
+
+def swap_out(pool, blocks, host, stream=None):
+    """Copy pool blocks (int32 device tensor) to a pinned host tensor laid out
+    [n][2][block_bytes] (K tile, then V tile, of each block)."""
+    _swap(pool, blocks, host, True, stream)
+
+
+def swap_in(pool, blocks, host, stream=None):
+    """Copy a pinned host tensor laid out as ``swap_out`` writes it into pool blocks."""
+    _swap(pool, blocks, host, False, stream)
+
+
 def decode_workspace_bytes(pool, num_seqs, q_heads, max_context_len, partition_tokens=0):
     """Workspace bytes ``decode`` needs; a new workspace must be zero-filled once before use."""
     out = ctypes.c_int64()
@@ -305,6 +329,28 @@ class BlockManager:
         check(lib().pa_bm_prefix_groups(self.handle, ids_ptr, n, starts_ptr, prefix_ptr, ctypes.addressof(ng),
                                         ctypes.addressof(mg)), "pa_bm_prefix_groups")
         return ng.value, mg.value
+
+    def _swap(self, seq_id, out):
+        n = ctypes.c_int32()
+        fn = lib().pa_bm_swap_out if out else lib().pa_bm_swap_in
+        name = "pa_bm_swap_out" if out else "pa_bm_swap_in"
+        buf = np.empty(1, dtype=np.int32)
+        code = fn(self.handle, int(seq_id), buf.ctypes.data, 0, ctypes.addressof(n))
+        if code == 0:                      # an empty table: done, no blocks
+            return np.empty(0, dtype=np.int32)
+        if code != -1:                     # -1: cap 0 was short; n now holds the table length
+            check(code, name)
+        buf = np.empty(max(n.value, 1), dtype=np.int32)
+        check(fn(self.handle, int(seq_id), buf.ctypes.data, buf.shape[0], ctypes.addressof(n)), name)
+        return buf[:n.value].copy()
+
+    def swap_out(self, seq_id):
+        """Swap a sequence out; returns its blocks in table order (the copy sources)."""
+        return self._swap(seq_id, True)
+
+    def swap_in(self, seq_id):
+        """Swap a sequence back in; returns its new blocks in table order (the copy destinations)."""
+        return self._swap(seq_id, False)
 
     def refcount(self, block):
         rc = ctypes.c_int32()

@@ -319,6 +319,62 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* s
   return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks launch");
 }
 
+// Shared checks of pa_swap_out / pa_swap_in; *host_dev receives the device
+// address of the pinned host buffer.
+static pa_status swap_args(const pa_pool* pool, const int32_t* blocks, int32_t n, const void* host,
+                           int64_t host_bytes, bool in, hipStream_t st, void** host_dev) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (n < 0) return fail(PA_ERR_INVALID, "n must be >= 0");
+  if (n == 0) return PA_OK;
+  if (!blocks || !host) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (host_bytes < static_cast<int64_t>(n) * 2 * pool->d.block_bytes)
+    return fail(PA_ERR_INVALID, "host buffer smaller than n x 2 x block_bytes");
+  if (!aligned(host, 16)) return fail(PA_ERR_INVALID, "host buffer must be 16-byte aligned");
+  // Two independent checks that the device may touch this memory: the
+  // runtime knows it as page-locked host memory, and maps it for the device.
+  hipPointerAttribute_t attr{};
+  hipError_t e = hipPointerGetAttributes(&attr, host);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID, "host buffer is not pinned host memory (hipHostMalloc or pin_memory=True)");
+  }
+  e = hipHostGetDevicePointer(host_dev, const_cast<void*>(host), 0);
+  if (e != hipSuccess || !*host_dev) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID, "host buffer is not mapped for the device");
+  }
+  if (debug_validate()) {
+    std::vector<int32_t> h;
+    if (pa_status s = fetch_ints(blocks, n, &h, st)) return s;
+    std::vector<char> seen(static_cast<size_t>(pool->d.num_blocks), 0);
+    for (int32_t i = 0; i < n; ++i) {
+      if (h[i] < 0 || h[i] >= pool->d.num_blocks) return fail(PA_ERR_INVALID, "block outside the pool");
+      if (in && seen[h[i]]++) return fail(PA_ERR_INVALID, "a block is swapped in twice");
+    }
+  }
+  return PA_OK;
+}
+
+pa_status pa_swap_out(const pa_pool* pool, const int32_t* blocks, int32_t n, void* host, int64_t host_bytes,
+                      void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* host_dev = nullptr;
+  if (pa_status s = swap_args(pool, blocks, n, host, host_bytes, false, st, &host_dev)) return s;
+  if (n == 0) return PA_OK;
+  hipError_t e = pa::launch_swap_blocks(pool->d, blocks, n, host_dev, true, st);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "swap_out launch");
+}
+
+pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void* host, int64_t host_bytes,
+                     void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* host_dev = nullptr;
+  if (pa_status s = swap_args(pool, blocks, n, host, host_bytes, true, st, &host_dev)) return s;
+  if (n == 0) return PA_OK;
+  hipError_t e = pa::launch_swap_blocks(pool->d, blocks, n, host_dev, false, st);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "swap_in launch");
+}
+
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
@@ -685,6 +741,37 @@ pa_status pa_bm_prefix_groups(const pa_bm* bm, const int64_t* seq_ids, int32_t n
                 why);
 }
 
+static pa_status bm_swap(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap, int32_t* n_blocks, bool out) {
+  if (!bm || !n_blocks || cap < 0 || (cap > 0 && !blocks)) return fail(PA_ERR_INVALID, "bad arguments");
+  // the table length is known before anything changes, so a short buffer changes nothing
+  int64_t need = 0;
+  if (out) {
+    const std::vector<int32_t>* t = bm->impl.table(seq_id, nullptr);
+    if (!t) return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seq_id));
+    need = static_cast<int64_t>(t->size());
+  } else {
+    const int32_t len = bm->impl.swapped_length(seq_id);
+    if (len < 0) return fail(PA_ERR_NOT_FOUND, "sequence " + std::to_string(seq_id) + " is not swapped out");
+    need = ceil_div(len, bm->impl.block_size());
+  }
+  *n_blocks = static_cast<int32_t>(need);
+  if (cap < need) return fail(PA_ERR_INVALID, "cap smaller than the block table");
+  std::vector<int32_t> got;
+  std::string why;
+  const pa::BmResult r = out ? bm->impl.swap_out(seq_id, &got, &why) : bm->impl.swap_in(seq_id, &got, &why);
+  if (r != pa::BmResult::ok) return map_bm(r, why);
+  if (!got.empty()) std::memcpy(blocks, got.data(), sizeof(int32_t) * got.size());
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap, int32_t* n_blocks) {
+  return bm_swap(bm, seq_id, blocks, cap, n_blocks, true);
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap, int32_t* n_blocks) {
+  return bm_swap(bm, seq_id, blocks, cap, n_blocks, false);
+}
+
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc) {
   if (!bm || !rc) return fail(PA_ERR_INVALID, "NULL pointer");
   if (block < 0 || block >= bm->impl.num_blocks()) return fail(PA_ERR_INVALID, "block outside the pool");
@@ -718,6 +805,9 @@ pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
   out->logical_blocks = s.logical_blocks;
   out->filled_slots = s.filled_slots;
   out->cow_copies = s.cow_copies;
+  out->swapped_seqs = s.swapped_seqs;
+  out->reserved = 0;
+  out->swapped_tokens = s.swapped_tokens;
   return PA_OK;
 }
 

@@ -42,7 +42,7 @@ BmResult BlockManager::add_seq(int64_t id, int32_t num_tokens, std::string* why)
     *why = "num_tokens must be >= 0";
     return BmResult::invalid;
   }
-  if (seqs_.count(id)) {
+  if (seqs_.count(id) || swapped_.count(id)) {
     *why = "sequence " + std::to_string(id) + " already exists";
     return BmResult::exists;
   }
@@ -65,7 +65,7 @@ BmResult BlockManager::fork(int64_t parent, int64_t child, std::string* why) {
     *why = "unknown parent " + std::to_string(parent);
     return BmResult::not_found;
   }
-  if (seqs_.count(child)) {
+  if (seqs_.count(child) || swapped_.count(child)) {
     *why = "sequence " + std::to_string(child) + " already exists";
     return BmResult::exists;
   }
@@ -245,7 +245,44 @@ BmResult BlockManager::prefix_groups(const int64_t* ids, int32_t n, int32_t* gro
   return BmResult::ok;
 }
 
+BmResult BlockManager::swap_out(int64_t id, std::vector<int32_t>* blocks, std::string* why) {
+  auto it = seqs_.find(id);
+  if (it == seqs_.end()) {
+    *why = "unknown sequence " + std::to_string(id);
+    return BmResult::not_found;
+  }
+  *blocks = it->second.table;
+  for (int32_t b : it->second.table) {
+    if (--rc_[b] == 0) free_.push_back(b);
+  }
+  swapped_[id] = it->second.length;
+  seqs_.erase(it);
+  return BmResult::ok;
+}
+
+BmResult BlockManager::swap_in(int64_t id, std::vector<int32_t>* blocks, std::string* why) {
+  auto it = swapped_.find(id);
+  if (it == swapped_.end()) {
+    *why = "sequence " + std::to_string(id) + " is not swapped out";
+    return BmResult::not_found;
+  }
+  const int64_t need = ceil_div(it->second, block_size_);
+  if (need > static_cast<int64_t>(free_.size())) {
+    *why = "swap-in needs " + std::to_string(need) + " blocks, " + std::to_string(free_.size()) + " free";
+    return BmResult::no_blocks;
+  }
+  Seq s;
+  s.length = it->second;
+  s.table.reserve(need);
+  for (int64_t j = 0; j < need; ++j) s.table.push_back(pop_free());
+  *blocks = s.table;
+  seqs_.emplace(id, std::move(s));
+  swapped_.erase(it);
+  return BmResult::ok;
+}
+
 BmResult BlockManager::free_seq(int64_t id, std::string* why) {
+  if (swapped_.erase(id)) return BmResult::ok;   // its blocks were released at swap-out
   auto it = seqs_.find(id);
   if (it == seqs_.end()) {
     *why = "unknown sequence " + std::to_string(id);
@@ -289,6 +326,8 @@ BmStats BlockManager::stats() const {
   }
   st.num_seqs = static_cast<int32_t>(seqs_.size());
   st.cow_copies = cow_copies_;
+  st.swapped_seqs = static_cast<int32_t>(swapped_.size());
+  for (const auto& kv : swapped_) st.swapped_tokens += kv.second;
   return st;
 }
 

@@ -23,6 +23,8 @@ enum class BmResult { ok, invalid, no_blocks, not_found, exists };
 struct BmStats {
   int32_t num_blocks, block_size, free_blocks, used_blocks, shared_blocks, num_seqs;
   int64_t logical_tokens, logical_blocks, filled_slots, cow_copies;
+  int32_t swapped_seqs, reserved;
+  int64_t swapped_tokens;
 };
 
 class BlockManager {
@@ -54,6 +56,21 @@ class BlockManager {
   BmResult prefix_groups(const int64_t* ids, int32_t n, int32_t* group_start, int32_t* prefix_tokens,
                          int32_t* num_groups, int32_t* max_group_size, std::string* why) const;
   BmResult free_seq(int64_t id, std::string* why);
+  // Swap a resident sequence out: *blocks receives its table (the blocks to
+  // copy to host memory, in order), each block's refcount drops (blocks
+  // reaching 0 join the free list in table order), and the sequence keeps
+  // only its length until swap_in.  A swapped sequence is unknown to every
+  // other call except free_seq.  cap < table length: invalid, no change.
+  BmResult swap_out(int64_t id, std::vector<int32_t>* blocks, std::string* why);
+  // Swap a sequence back in: it takes ⌈length / block_size⌉ blocks from the
+  // free list (all private, refcount 1), returned in table order as the
+  // destinations of the copy back.  Not enough free blocks: no change.
+  BmResult swap_in(int64_t id, std::vector<int32_t>* blocks, std::string* why);
+  // Length of a swapped-out sequence, or -1 if id is not swapped out.
+  int32_t swapped_length(int64_t id) const {
+    auto it = swapped_.find(id);
+    return it == swapped_.end() ? -1 : it->second;
+  }
 
   const std::vector<int32_t>* table(int64_t id, int32_t* length) const;
   int32_t refcount(int32_t block) const { return rc_[block]; }
@@ -75,6 +92,7 @@ class BlockManager {
   std::deque<int32_t> free_;
   std::vector<int32_t> rc_;
   std::unordered_map<int64_t, Seq> seqs_;
+  std::unordered_map<int64_t, int32_t> swapped_;   // id -> length of swapped-out sequences
   int64_t cow_copies_ = 0;
   std::vector<int32_t> drop_scratch_;  // per-block refcount drops during a step's dry run
 };

@@ -1,10 +1,11 @@
-// Slot-mapped KV write and copy-on-write block copy for gfx950.
+// Slot-mapped KV write, copy-on-write block copy and block swap for gfx950.
 //
 // [P2] "PagedAttention：操作系统级 KV 缓存虚拟内存管理" §3.2.2 step 3 (the new
-// token's K/V goes into its slot) and §3.4 (a shared block is copied before a
-// divergent write).  Both are pure byte moves: every lane moves one 16-byte
-// vector, consecutive lanes move consecutive bytes of a token row or block, so
-// each wavefront issues fully coalesced 1 KiB global loads and stores.
+// token's K/V goes into its slot), §3.4 (a shared block is copied before a
+// divergent write) and §5 / §8 (inactive blocks move out to CPU memory and
+// back, as pages are swapped).  All are pure byte moves: every lane moves one
+// 16-byte vector, consecutive lanes move consecutive bytes of a token row or
+// block, so each wavefront issues fully coalesced 1 KiB loads and stores.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -60,7 +61,54 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict_
   }
 }
 
+// Grid: x = block × chunk-groups, y = tensor (K, V).  Host layout: block i's
+// K tile (all kv-heads) then its V tile, [n][2][block_bytes].  OUT moves pool
+// → host, else host → pool; the host side is pinned memory the device maps,
+// so the bytes cross the host link once, with no staging copy in HBM.  Block
+// ids outside the pool are skipped.
+template <bool OUT>
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                                               char* __restrict__ host,
+                                                               const int32_t* __restrict__ blocks,
+                                                               int32_t groups_per_block, int64_t block_bytes,
+                                                               int32_t num_blocks) {
+  const int32_t i = blockIdx.x / groups_per_block;
+  const int32_t grp = blockIdx.x - i * groups_per_block;
+  const int32_t b = blocks[i];
+  if (b < 0 || b >= num_blocks) return;
+  char* pool_blk = (blockIdx.y ? v_pool : k_pool) + static_cast<int64_t>(b) * block_bytes;
+  char* host_blk = host + (2 * static_cast<int64_t>(i) + blockIdx.y) * block_bytes;
+  const int64_t stride = static_cast<int64_t>(groups_per_block) * kThreads * 16;
+  for (int64_t off = (static_cast<int64_t>(grp) * kThreads + threadIdx.x) * 16; off < block_bytes; off += stride) {
+    if constexpr (OUT) {
+      *reinterpret_cast<uint4*>(host_blk + off) = *reinterpret_cast<const uint4*>(pool_blk + off);
+    } else {
+      *reinterpret_cast<uint4*>(pool_blk + off) = *reinterpret_cast<const uint4*>(host_blk + off);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swap_blocks(const PoolDesc& p, const int32_t* blocks, int32_t n, void* host_dev, bool out,
+                              hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t chunks = p.block_bytes / 16;
+  int32_t groups = static_cast<int32_t>((chunks + kThreads - 1) / kThreads);
+  if (groups > 16) groups = 16;
+  const int64_t grid = static_cast<int64_t>(n) * groups;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (out) {
+    hipLaunchKernelGGL(swap_blocks_kernel<true>, dim3(static_cast<uint32_t>(grid), 2), dim3(kThreads), 0, stream,
+                       static_cast<char*>(p.k), static_cast<char*>(p.v), static_cast<char*>(host_dev), blocks,
+                       groups, p.block_bytes, p.num_blocks);
+  } else {
+    hipLaunchKernelGGL(swap_blocks_kernel<false>, dim3(static_cast<uint32_t>(grid), 2), dim3(kThreads), 0, stream,
+                       static_cast<char*>(p.k), static_cast<char*>(p.v), static_cast<char*>(host_dev), blocks,
+                       groups, p.block_bytes, p.num_blocks);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_write_kv(const PoolDesc& p, const void* k_new, const void* v_new, const int32_t* slots,
                            int32_t n, hipStream_t stream) {

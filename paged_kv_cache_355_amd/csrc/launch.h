@@ -71,6 +71,9 @@ bool decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32
 hipError_t launch_write_kv(const PoolDesc& p, const void* k_new, const void* v_new, const int32_t* slots,
                            int32_t n, hipStream_t stream);
 hipError_t launch_copy_blocks(const PoolDesc& p, const int32_t* pairs, int32_t n, hipStream_t stream);
+// host_dev: the device address of pinned host memory of n × 2 × block_bytes.
+hipError_t launch_swap_blocks(const PoolDesc& p, const int32_t* blocks, int32_t n, void* host_dev, bool out,
+                              hipStream_t stream);
 hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 
 // Workgroups of the balanced decode kernel for these sizes (every one

@@ -9,7 +9,10 @@
 //   * a copy-on-write pair copies the writer's old last block into a block
 //     that was free, and calls that fail change nothing;
 //   * a dispatch order is a permutation of the batch positions with groups
-//     (same first block) contiguous and longest members never rising.
+//     (same first block) contiguous and longest members never rising;
+//   * swap-out returns the table and releases it; swap-in takes blocks from
+//     the head of the free list, private, as many as the length needs, and a
+//     failed swap-in changes nothing.
 // Exit status 0 means every check held; a sanitizer report aborts.
 #include <algorithm>
 #include <cstdio>
@@ -92,6 +95,7 @@ int main(int argc, char** argv) {
     std::shuffle(order.begin(), order.end(), rng);
     BlockManager bm(nb, bs, order);
     std::set<int64_t> ids;
+    std::map<int64_t, int32_t> swapped;   // id -> length
     int64_t next_id = 0;
     std::string why;
     for (int it = 0; it < iters; ++it) {
@@ -170,16 +174,49 @@ int main(int argc, char** argv) {
         CHECK(bm.fork(next_id + 9, next_id + 10, &why) == BmResult::not_found);
         CHECK(bm.free_seq(next_id + 11, &why) == BmResult::not_found);
         CHECK(same(before, snap(bm, ids)));
-      } else if (!ids.empty()) {  // release
+      } else if (op < 90 && !ids.empty()) {  // swap out
         auto p = ids.begin();
         std::advance(p, static_cast<long>(rng() % ids.size()));
-        CHECK(bm.free_seq(*p, &why) == BmResult::ok);
+        int32_t len = 0;
+        const std::vector<int32_t> table = *bm.table(*p, &len);
+        std::vector<int32_t> blocks;
+        CHECK(bm.swap_out(*p, &blocks, &why) == BmResult::ok);
+        CHECK(blocks == table && bm.table(*p, nullptr) == nullptr && bm.swapped_length(*p) == len);
+        swapped[*p] = len;
         ids.erase(p);
+      } else if (op < 95 && !swapped.empty()) {  // swap in
+        auto p = swapped.begin();
+        std::advance(p, static_cast<long>(rng() % swapped.size()));
+        const std::vector<int32_t> free_before(bm.free_list().begin(), bm.free_list().end());
+        std::vector<int32_t> blocks;
+        const BmResult r = bm.swap_in(p->first, &blocks, &why);
+        const size_t need = static_cast<size_t>((static_cast<int64_t>(p->second) + bs - 1) / bs);
+        if (r == BmResult::ok) {
+          CHECK(blocks.size() == need);
+          CHECK(std::equal(blocks.begin(), blocks.end(), free_before.begin()));
+          for (int32_t b : blocks) CHECK(bm.refcount(b) == 1);
+          ids.insert(p->first);
+          swapped.erase(p);
+        } else {
+          CHECK(r == BmResult::no_blocks && need > free_before.size() && same(before, snap(bm, ids)));
+        }
+      } else if (!ids.empty() || !swapped.empty()) {  // release (resident or swapped)
+        if (!swapped.empty() && (ids.empty() || rng() % 4 == 0)) {
+          auto p = swapped.begin();
+          CHECK(bm.free_seq(p->first, &why) == BmResult::ok);
+          swapped.erase(p);
+        } else {
+          auto p = ids.begin();
+          std::advance(p, static_cast<long>(rng() % ids.size()));
+          CHECK(bm.free_seq(*p, &why) == BmResult::ok);
+          ids.erase(p);
+        }
       }
       check_invariants(bm, ids);
     }
     const pa::BmStats st = bm.stats();
     CHECK(st.free_blocks + st.used_blocks == nb);
+    CHECK(st.swapped_seqs == static_cast<int32_t>(swapped.size()));
   }
   std::printf("bm_fuzz: %d failed checks\n", g_fail);
   return g_fail == 0 ? 0 : 1;

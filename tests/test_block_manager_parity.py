@@ -19,6 +19,9 @@ def assert_same_state(lib_bm, ora):
     assert [lib_bm.refcount(b) for b in range(ora.num_blocks)] == ora.rc
     for sid in ora.seqs:
         assert lib_bm.block_table(sid) == ora.block_table(sid)
+    for sid in ora.swapped:
+        with pytest.raises(pk.PaError):
+            lib_bm.block_table(sid)
     st_ = lib_bm.stats()
     ost = ora.stats()
     for k, v in ost.items():
@@ -94,6 +97,34 @@ def test_step_rejects_short_stride_without_change():
     assert lib_bm.block_table(0) == before
 
 
+def test_swap_calls_and_errors():
+    lib_bm = pk.BlockManager(8, 4)
+    lib_bm.add_seq(1, 9)
+    lib_bm.add_seq(2, 0)
+    assert lib_bm.swap_out(2).tolist() == [] and lib_bm.swap_in(2).tolist() == []
+    blocks = lib_bm.swap_out(1)
+    assert blocks.tolist() == [0, 1, 2] and lib_bm.stats()["swapped_seqs"] == 1
+    for call in (lambda: lib_bm.swap_out(1), lambda: lib_bm.step([1]), lambda: lib_bm.fork(1, 5),
+                 lambda: lib_bm.dispatch_order([1]), lambda: lib_bm.swap_in(7)):
+        with pytest.raises(pk.PaError) as e:
+            call()
+        assert e.value.code == -5                                     # PA_ERR_NOT_FOUND
+    with pytest.raises(pk.PaError) as e:
+        lib_bm.add_seq(1, 3)
+    assert e.value.code == -6                                         # PA_ERR_EXISTS
+    lib_bm.add_seq(3, 24)                                             # takes 6 of the 8 blocks
+    with pytest.raises(pk.NoBlocksError):
+        lib_bm.swap_in(1)                                             # needs 3, 2 free: no change
+    assert lib_bm.stats()["swapped_seqs"] == 1
+    lib_bm.free_seq(3)
+    back = lib_bm.swap_in(1)
+    assert len(back) == 3 and lib_bm.block_table(1)[1] == 9
+    lib_bm.free_seq(1)
+    lib_bm.swap_out(2)
+    lib_bm.free_seq(2)                                                # a swapped sequence can be freed
+    assert lib_bm.stats()["swapped_seqs"] == 0 and lib_bm.stats()["free_blocks"] == 8
+
+
 def test_bad_calls():
     bm = pk.BlockManager(8, 4)
     bm.add_seq(1, 3)
@@ -166,8 +197,26 @@ class ParityMachine(RuleBasedStateMachine):
 
     @precondition(lambda self: self.ora.seqs)
     @rule(data=st.data())
-    def free(self, data):
+    def swap_out(self, data):
         sid = data.draw(st.sampled_from(sorted(self.ora.seqs)))
+        assert self.lib.swap_out(sid).tolist() == self.ora.swap_out(sid)
+
+    @precondition(lambda self: self.ora.swapped)
+    @rule(data=st.data())
+    def swap_in(self, data):
+        sid = data.draw(st.sampled_from(sorted(self.ora.swapped)))
+        try:
+            want = self.ora.swap_in(sid)
+        except NoBlocksError:
+            with pytest.raises(pk.NoBlocksError):
+                self.lib.swap_in(sid)
+            return
+        assert self.lib.swap_in(sid).tolist() == want
+
+    @precondition(lambda self: self.ora.seqs or self.ora.swapped)
+    @rule(data=st.data())
+    def free(self, data):
+        sid = data.draw(st.sampled_from(sorted(list(self.ora.seqs) + list(self.ora.swapped))))
         self.ora.free_seq(sid)
         self.lib.free_seq(sid)
 

@@ -168,7 +168,10 @@ def test_sharing_ratio_and_utilisation():
 
 
 class BMStateMachine(RuleBasedStateMachine):
-    """Random add/fork/step/free sequences; invariants hold after every call."""
+    """Random add/fork/step/swap/free sequences; invariants hold after every call.
+    A swap moves the simulated pool's tags of the returned blocks to a host copy
+    and back into the blocks swap-in returns, so the read-back invariant checks
+    that a sequence comes back with its own tokens in order."""
 
     def __init__(self):
         super().__init__()
@@ -178,6 +181,7 @@ class BMStateMachine(RuleBasedStateMachine):
         self.next_id = 0
         self.contents = {}   # seq id → list of token tags, in logical order
         self.slot_tag = {}   # flat slot → tag written there (a simulated pool)
+        self.host = {}       # swapped seq id → tags of its blocks, in table order
 
     def _write(self, seq, t, slot):
         tag = (seq, t, self.next_id)
@@ -227,10 +231,37 @@ class BMStateMachine(RuleBasedStateMachine):
 
     @precondition(lambda self: self.bm.seqs)
     @rule(data=st.data())
-    def free(self, data):
+    def swap_out(self, data):
         sid = data.draw(st.sampled_from(sorted(self.bm.seqs)))
+        table = self.bm.block_table(sid)[0]
+        blocks = self.bm.swap_out(sid)
+        assert blocks == table and sid not in self.bm.seqs
+        self.host[sid] = [[self.slot_tag.get(b * self.bs + o) for o in range(self.bs)] for b in blocks]
+
+    @precondition(lambda self: self.bm.swapped)
+    @rule(data=st.data())
+    def swap_in(self, data):
+        sid = data.draw(st.sampled_from(sorted(self.bm.swapped)))
+        free_before = list(self.bm.free)
+        try:
+            blocks = self.bm.swap_in(sid)
+        except NoBlocksError:
+            assert list(self.bm.free) == free_before and sid in self.bm.swapped
+            return
+        assert blocks == free_before[:len(blocks)]                   # taken from the head of the free list
+        assert all(self.bm.refcount(b) == 1 for b in blocks)
+        for b, tags in zip(blocks, self.host.pop(sid)):
+            for o, tag in enumerate(tags):
+                if tag is not None:
+                    self.slot_tag[b * self.bs + o] = tag
+
+    @precondition(lambda self: self.bm.seqs or self.bm.swapped)
+    @rule(data=st.data())
+    def free(self, data):
+        sid = data.draw(st.sampled_from(sorted(list(self.bm.seqs) + list(self.bm.swapped))))
         self.bm.free_seq(sid)
         del self.contents[sid]
+        self.host.pop(sid, None)
 
     @invariant()
     def refcounts_match_owners(self):
@@ -246,6 +277,13 @@ class BMStateMachine(RuleBasedStateMachine):
         assert len(set(free)) == len(free)
         used = {b for b in range(self.nb) if self.bm.refcount(b) > 0}
         assert used.isdisjoint(free) and used | set(free) == set(range(self.nb))
+
+    @invariant()
+    def swapped_sequences_hold_no_blocks(self):
+        assert set(self.bm.swapped).isdisjoint(self.bm.seqs)
+        st_ = self.bm.stats()
+        assert st_["swapped_seqs"] == len(self.bm.swapped)
+        assert st_["swapped_tokens"] == sum(len(self.contents[s]) for s in self.bm.swapped)
 
     @invariant()
     def tables_cover_lengths(self):
@@ -402,3 +440,30 @@ def test_prefix_groups_properties(spec, rnd):
         grow_ok = (all(bm.length(s) >= p + bs for s in members) and
                    all(len(t) > nb and t[nb] == tables[0][nb] for t in tables))
         assert not grow_ok
+
+
+def test_swap_hand_example(example):
+    """The worked example's sequence (10 tokens in blocks 5, 12, 3) swapped out
+    and back: the blocks come back in table order and rejoin the free tail;
+    swap-in takes the head of the free list.  A forked sharer's swap-out only
+    drops refcounts, and it comes back with private blocks."""
+    bs = example["block_size"]
+    table = example["block_table"]
+    order = table + [b for b in range(16) if b not in table]
+    bm = OracleBlockManager(16, bs, order)
+    bm.add_seq(0, example["num_tokens"])
+    head = list(bm.free)[:3]
+    assert bm.swap_out(0) == table
+    assert list(bm.free)[-3:] == table and bm.stats()["swapped_seqs"] == 1
+    assert bm.stats()["swapped_tokens"] == example["num_tokens"]
+    with pytest.raises(KeyError):
+        bm.block_table(0)
+    assert bm.swap_in(0) == head
+    assert bm.block_table(0) == (head, example["num_tokens"])
+    bm.fork(0, 1)
+    assert all(bm.refcount(b) == 2 for b in head)
+    assert bm.swap_out(1) == head and all(bm.refcount(b) == 1 for b in head)
+    back = bm.swap_in(1)
+    assert set(back).isdisjoint(head) and all(bm.refcount(b) == 1 for b in back)
+    with pytest.raises(KeyError):
+        bm.swap_in(1)                                                 # not swapped out any more

@@ -84,3 +84,22 @@ def test_copy_empty_is_noop():
     k0 = k.copy()
     copy_blocks(k, v, [])
     assert np.array_equal(k, k0)
+
+
+def test_swap_out_layout_and_round_trip():
+    """Every element tagged with (block, head, slot, dim) in K and the same
+    plus an offset in V: swap_out returns [n][K, V] tiles in the order asked,
+    and swap_in writes them back into other blocks unchanged."""
+    from oracle.kv_ops import swap_out, swap_in
+    nb, hkv, bs, d = 6, 2, 4, 3
+    idx = np.arange(nb * hkv * bs * d, dtype=np.uint32).reshape(nb, hkv, bs, d)
+    k, v = idx.copy(), idx + np.uint32(1 << 20)
+    host = swap_out(k, v, [4, 1])
+    assert host.shape == (2, 2, hkv, bs, d)
+    assert np.array_equal(host[0, 0], idx[4]) and np.array_equal(host[1, 1], idx[1] + (1 << 20))
+    k2, v2 = np.zeros_like(k), np.zeros_like(v)
+    swap_in(k2, v2, [0, 5], host)
+    assert np.array_equal(k2[0], k[4]) and np.array_equal(v2[5], v[1])
+    assert not k2[1:5].any() and not v2[1:5].any()
+    with pytest.raises(ValueError):
+        swap_in(k2, v2, [2, 2], host)
