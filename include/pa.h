@@ -242,7 +242,9 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
  *     prefixes and the rest; 0 = whole contexts when the batch fills the
  *     device, else 512.  PA_PARTITION_BALANCED is rejected.
  *   workspace: ≥ pa_decode_shared_prefix_workspace_bytes(...) bytes, 256-byte
- *     aligned (partial results; no zero-fill needed).
+ *     aligned, zero-filled once before first use as for pa_decode (the
+ *     shared-prefix kernels only write partial results there; the fallback
+ *     below may take pa_decode's balanced split, whose counters live there).
  * Pools with fp32 K/V or blocks under 16 tokens, and max_prefix_tokens = 0,
  * take pa_decode itself (the grouping arguments are then ignored).  A
  * violated grouping contract gives wrong rows, never an out-of-bounds
