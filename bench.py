@@ -53,6 +53,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="attention layers per step, one KV pool each")
     ap.add_argument("--workload", default="mha7b_fp16")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="a smaller batch of the workload's sequences (default: the workload's own batch)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0 = the workload's setting (the library's automatic choice unless it names fixed "
                          "partitions); -1 = the balanced split; > 0 = fixed partitions of that many tokens")
@@ -446,7 +448,7 @@ def main():
     torch.cuda.set_device(0)
     pk.lib()
     w = WORKLOADS[args.workload]
-    sc = make_scenario(w)
+    sc = make_scenario(w, batch=args.batch)
     steps_total = args.warmup + args.steps
     log(f"[bench] workload {w.name}: B={len(sc.measured)} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} "
         f"{w.dtype} bs={w.block_size} pool={sc.num_blocks} blocks x {args.layers} layers")
