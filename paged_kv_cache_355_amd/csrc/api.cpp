@@ -94,7 +94,7 @@ int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 // How to split: an explicit positive partition length (a multiple of
 // block_size) or PA_PARTITION_BALANCED; for 0, the PA_PARTITION_TOKENS
 // override, else whole sequences (one workgroup per (sequence, kv-head),
-// longest first) when the batch's units fill the device, else the balanced
+// in batch order) when the batch's units fill the device, else the balanced
 // split.
 pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
                       int32_t requested, DecodePlan* plan) {
@@ -179,6 +179,25 @@ pa_status plan_shared_prefix(const pa_pool* pool, int32_t num_seqs, int32_t q_he
   plan->o_off = round256(rows * 2 * 4);
   plan->bytes = plan->o_off + rows * d.head_dim * 4;
   return PA_OK;
+}
+
+// The arguments every decode launch shares; scale ≤ 0 selects 1/sqrt(head_dim).
+pa::DecodeArgs decode_args(const pa::PoolDesc& d, void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs,
+                           int32_t q_heads, const int32_t* block_tables, int32_t stride, const int32_t* context_lens,
+                           int32_t max_context_len, float scale) {
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.block_tables = block_tables;
+  a.table_stride = stride;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d.head_dim));
+  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);  // log2(e)
+  return a;
 }
 
 // Host checks of pa_decode's device-resident indices (PA_DEBUG_VALIDATE).
@@ -449,18 +468,8 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
           return fail(PA_ERR_INVALID, "workspace merge counters are not zero (zero-fill a new workspace once)");
     }
   }
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.q = q;
-  a.num_seqs = num_seqs;
-  a.q_heads = q_heads;
-  a.block_tables = block_tables;
-  a.table_stride = block_table_stride;
-  a.context_lens = context_lens;
-  a.max_context_len = max_context_len;
-  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d.head_dim));
-  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);  // log2(e)
+  pa::DecodeArgs a = decode_args(d, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride,
+                                 context_lens, max_context_len, scale);
   a.balanced = plan.balanced;
   a.grid = plan.grid;
   a.num_slots = plan.num_slots;
@@ -566,18 +575,8 @@ pa_status pa_decode_shared_prefix(const pa_pool* pool, void* out, pa_dtype out_d
       }
     }
   }
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.q = q;
-  a.num_seqs = num_seqs;
-  a.q_heads = q_heads;
-  a.block_tables = block_tables;
-  a.table_stride = block_table_stride;
-  a.context_lens = context_lens;
-  a.max_context_len = max_context_len;
-  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d.head_dim));
-  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);  // log2(e)
+  pa::DecodeArgs a = decode_args(d, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride,
+                                 context_lens, max_context_len, scale);
   a.partition_tokens = plan.partition_tokens;
   a.max_parts = plan.max_parts;
   char* ws = static_cast<char*>(workspace);

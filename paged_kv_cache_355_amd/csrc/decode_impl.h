@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
 }
 
 // ---------------------------------------------------------------------------
-// Balanced split (the default)
+// Balanced split (the automatic choice when the batch does not fill the device)
 // ---------------------------------------------------------------------------
 
 // Chunks of CT tokens a sequence of length len contributes per kv-head
