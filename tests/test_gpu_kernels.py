@@ -342,3 +342,21 @@ def test_decode_empty_batch_and_argument_errors(gpu):
         pk.decode(pool, torch.zeros((1, 2, 128), dtype=torch.float16, device="cuda"),
                   torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
                   torch.ones((1,), dtype=torch.int32, device="cuda"), 1, partition_tokens=24)
+
+
+@pytest.mark.parametrize("partition", [0, -1, 4])
+def test_decode_maximum_batch(gpu, partition):
+    """65535 sequences (the largest batch the ABI takes: one grid dimension)
+    of 0-9 tokens, in every split mode; sampled rows against the oracle,
+    empty rows exactly zero."""
+    pk = gpu
+    rng = np.random.default_rng(65535)
+    lens = [int(x) for x in rng.integers(0, 10, size=65535)]
+    case = build_case(lens, 2, 2, 64, 4, "f16", 7, extra_blocks=2)
+    got = out_to_f64(run_decode(pk, case, 2, 64, 4, "f16", out_dtype="f32", partition_tokens=partition))
+    picks = sorted(set([0, 65534] + [int(i) for i in rng.integers(0, 65535, size=300)]))
+    want = paged_decode(case["q"][picks], case["k_pool"], case["v_pool"], case["tables"][picks],
+                        case["lens"][picks], "f16")
+    assert np.max(np.abs(got[picks] - want)) <= TOL["f16"]
+    assert np.all(got[np.array(lens) == 0] == 0.0)
+    assert np.all(np.isfinite(got))
