@@ -1113,6 +1113,14 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
 // Balanced split (the automatic choice when the batch does not fill the device)
 // ---------------------------------------------------------------------------
 
+// A value every lane of the wave holds alike, moved to scalar registers (the
+// compiler cannot know that a value read back from LDS is uniform).
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Chunks of CT tokens a sequence of length len contributes per kv-head
 // (0 for an empty or invalid length).
 template <int CT>
@@ -1287,7 +1295,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
     block_exclusive_scan<NW>(thread_chunks(base, ck), &round_total, sh_scan);
     total += round_total;
   }
-  const int64_t C = total * kv_heads;
+  const int64_t C = uniform(total) * kv_heads;
   // Workgroups past the chunk count sit out, so every slice holds at least one
   // chunk and a unit's pieces are exactly the workgroups its chunks span.
   const int64_t W = min(static_cast<int64_t>(gridDim.x), C);
@@ -1324,8 +1332,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
   }
 
   // Walk the units that meet [start, end).
-  int32_t s = static_cast<int32_t>(sh_found[0]);
-  int64_t P = sh_found[1];
+  int32_t s = static_cast<int32_t>(uniform(sh_found[0]));
+  int64_t P = uniform(sh_found[1]);
   __shared__ int sh_last;
   __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
   for (; s < num_seqs; ++s) {
@@ -1344,15 +1352,9 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
       const int64_t b = min(end, off + c) - off;
       const int32_t t0 = static_cast<int32_t>(a * CT);
       const int32_t t1 = static_cast<int32_t>(min(b * CT, static_cast<int64_t>(len)));
-      if (a == 0 && b == c) {   // the whole unit: write the output directly
-        attend_range_policy<DT, D, BS, G, NW>(
-            shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
-            [&](int r, int d, float M, float L, float O, bool bad) {
-              const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
-              store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
-            });
-        continue;
-      }
+      // A whole unit writes its output; a piece writes a record and climbs the
+      // merge tree.  One call site for both keeps a single copy of the loop.
+      const bool whole = a == 0 && b == c;
       const int64_t u = static_cast<int64_t>(s) * kv_heads + g;
       const int64_t first_w = slice_owner(off, C, W);
       const int64_t slot0 = u + first_w;
@@ -1362,6 +1364,11 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
       attend_range_policy<DT, D, BS, G, NW>(
           shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
           [&](int r, int d, float M, float L, float O, bool bad) {
+            if (whole) {
+              const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
+              store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : 0.f));
+              return;
+            }
             const int64_t rr = my_slot * G + r;
             st_rec(rec_o + rr * D + d, O);
             if (d == 0) {
@@ -1369,6 +1376,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
               st_rec(rec_ml + rr * 2 + 1, bad ? qnan() : L);
             }
           });
+      if (whole) continue;
       // Climb the merge tree while this workgroup is the last child to finish.
       int64_t span = 1;
       for (int level = 0; level < kMaxLevels; ++level) {
@@ -1398,8 +1406,6 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
 // Host-side launch
 // ---------------------------------------------------------------------------
 
-// Workgroups of the balanced kernel: every one resident at once (occupancy ×
-// CUs), at most one per chunk the batch can hold, or PA_DECODE_GRID.
 // Workgroups of the fixed-partition kernel that fit on the current device at once.
 template <int DT, int D, int BS, int G>
 hipError_t partition_resident(int32_t* resident_out) {
@@ -1423,6 +1429,8 @@ hipError_t partition_resident(int32_t* resident_out) {
   return hipSuccess;
 }
 
+// Workgroups of the balanced kernel: every one resident at once (occupancy ×
+// CUs), at most one per chunk the batch can hold, or PA_DECODE_GRID.
 template <int DT, int D, int BS, int G>
 hipError_t balanced_grid(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
   constexpr int CT = Chunk<DT, D, BS>::CT;
