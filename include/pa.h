@@ -142,12 +142,14 @@ pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32
                                     int32_t max_context_len, int32_t partition_tokens,
                                     int64_t* bytes);
 
-/* partition_tokens value that selects the balanced split (see pa_decode). */
+/* partition_tokens values that select the balanced and the uniform split
+ * (see pa_decode). */
 #define PA_PARTITION_BALANCED -1
+#define PA_PARTITION_UNIFORM -2
 
 /* How pa_decode will split these sizes: the partition length in tokens (a
- * length ≥ max_context_len means one workgroup per (sequence, kv-head)), or
- * PA_PARTITION_BALANCED. */
+ * length ≥ max_context_len means one workgroup per (sequence, kv-head)),
+ * PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM. */
 pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
                                      int32_t max_context_len, int32_t partition_tokens,
                                      int32_t* resolved);
@@ -191,6 +193,12 @@ pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void
  *       > 0 — fixed partitions of that many tokens (a multiple of
  *           block_size), one workgroup each, merged by a second reduce
  *           kernel when a sequence has more than one;
+ *       PA_PARTITION_UNIFORM — one grid of workgroups, all resident at
+ *           once; the device picks the shortest partition length (a
+ *           multiple of block_size) whose partitions of every (sequence,
+ *           kv-head) unit fit in that grid, numbers them densely and runs
+ *           one per workgroup, so every XCD gets an equal count; units of
+ *           more than one partition are merged by the reduce kernel;
  *       PA_PARTITION_BALANCED — one grid of workgroups, all resident at
  *           once, each taking an equal share of the batch's total KV; pieces
  *           of a sequence that straddle workgroups are merged inside the
@@ -198,7 +206,7 @@ pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void
  *       0 — automatic: PA_PARTITION_TOKENS if set and positive; else, when
  *           the batch has at least as many (sequence, kv-head) units as the
  *           device holds workgroups at once, one workgroup per unit with no
- *           split; else the balanced split.
+ *           split; else the uniform split.
  *     With fixed partitions (and in the automatic whole-sequence case)
  *     workgroups start in batch order, sequence 0 first; arrange the batch
  *     with pa_bm_dispatch_order to run long sequences first.  Results do not

@@ -21,6 +21,7 @@ PA_ERR_NO_MEMORY = -8
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_PARTITION_BALANCED = -1
+PA_PARTITION_UNIFORM = -2
 
 c_i32 = ctypes.c_int32
 c_i64 = ctypes.c_int64

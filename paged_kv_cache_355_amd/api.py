@@ -135,7 +135,8 @@ def decode_workspace_bytes(pool, num_seqs, q_heads, max_context_len, partition_t
 
 
 def decode_partition_tokens(pool, num_seqs, q_heads, max_context_len, partition_tokens=0):
-    """Partition length ``decode`` will use (PA_PARTITION_BALANCED = -1 for the balanced split)."""
+    """Partition length ``decode`` will use (PA_PARTITION_BALANCED = -1 for the balanced split,
+    PA_PARTITION_UNIFORM = -2 for the uniform split)."""
     out = ctypes.c_int32()
     check(lib().pa_decode_partition_tokens(pool.handle, num_seqs, q_heads, max_context_len, partition_tokens,
                                            ctypes.addressof(out)), "pa_decode_partition_tokens")

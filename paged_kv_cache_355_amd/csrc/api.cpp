@@ -82,6 +82,8 @@ pa_status fetch_ints(const int32_t* dev, int64_t n, std::vector<int32_t>* host, 
 // pieces sit.
 struct DecodePlan {
   bool balanced = false;
+  bool uniform = false;          // uniform split: `grid` workgroups, unit descriptors at desc_off
+  int64_t desc_off = 0;
   int32_t partition_tokens = 0;  // fixed partitions
   int32_t max_parts = 1;
   int32_t grid = 0;              // balanced split
@@ -92,15 +94,15 @@ struct DecodePlan {
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // How to split: an explicit positive partition length (a multiple of
-// block_size) or PA_PARTITION_BALANCED; for 0, the PA_PARTITION_TOKENS
-// override, else whole sequences (one workgroup per (sequence, kv-head),
-// in batch order) when the batch's units fill the device, else the balanced
-// split.
+// block_size), PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM; for 0, the
+// PA_PARTITION_TOKENS override, else whole sequences (one workgroup per
+// (sequence, kv-head), in batch order) when the batch's units fill the
+// device, else the uniform split.
 pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, int32_t max_context_len,
                       int32_t requested, DecodePlan* plan) {
   const pa::PoolDesc& d = pool->d;
-  if (requested < 0 && requested != PA_PARTITION_BALANCED)
-    return fail(PA_ERR_INVALID, "partition_tokens must be >= 0 or PA_PARTITION_BALANCED");
+  if (requested < 0 && requested != PA_PARTITION_BALANCED && requested != PA_PARTITION_UNIFORM)
+    return fail(PA_ERR_INVALID, "partition_tokens must be >= 0, PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM");
   *plan = DecodePlan{};
   if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
     return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
@@ -108,12 +110,17 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
   const int32_t group = q_heads / d.kv_heads;
   const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
   int32_t p = requested > 0 ? requested : (requested == 0 ? env_int("PA_PARTITION_TOKENS", 0) : 0);
-  int32_t grid = 0, capacity = 0;
+  pa::DecodeCapacity cap{};
+  bool uniform = requested == PA_PARTITION_UNIFORM;
   if (p <= 0) {
-    hipError_t e = pa::decode_balanced_grid(d, group, num_seqs, max_context_len, &grid, &capacity);
+    hipError_t e = pa::decode_capacity(d, group, num_seqs, max_context_len, &cap);
     if (e != hipSuccess) return hip_fail(e, "decode grid query");
-    if (requested == 0 && units >= capacity)   // whole sequences keep every CU busy
-      p = static_cast<int32_t>(ceil_div(std::max(max_context_len, 1), d.block_size) * d.block_size);
+    if (requested == 0) {
+      if (units >= cap.partition)   // whole sequences keep every CU busy
+        p = static_cast<int32_t>(ceil_div(std::max(max_context_len, 1), d.block_size) * d.block_size);
+      else
+        uniform = true;
+    }
   }
   if (p > 0) {
     if (p % d.block_size != 0)
@@ -129,6 +136,25 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
     }
     return PA_OK;
   }
+  if (uniform) {
+    // One resident grid (PA_DECODE_GRID overrides), at least one workgroup
+    // per unit, at most one per block of every unit.
+    int64_t W = cap.uniform;
+    const int32_t forced = env_int("PA_DECODE_GRID", 0);
+    if (forced > 0) W = forced;
+    W = std::min<int64_t>(W, units * std::max<int64_t>(1, ceil_div(max_context_len, d.block_size)));
+    W = std::max<int64_t>(W, units);
+    if (W >= (int64_t{1} << 31)) return fail(PA_ERR_INVALID, "too many sequences x kv-heads");
+    plan->uniform = true;
+    plan->grid = static_cast<int32_t>(W);
+    const int64_t rows = W * group;
+    plan->ml_off = 0;
+    plan->o_off = round256(rows * 2 * 4);
+    plan->desc_off = round256(plan->o_off + rows * d.head_dim * 4);
+    plan->bytes = plan->desc_off + units * 2 * 4;
+    return PA_OK;
+  }
+  const int32_t grid = cap.balanced_grid;
   plan->balanced = true;
   if (units * std::max<int64_t>(max_context_len, 1) >= (int64_t{1} << 40))
     return fail(PA_ERR_INVALID, "num_seqs * kv_heads * max_context_len must be < 2^40");
@@ -162,12 +188,13 @@ pa_status plan_shared_prefix(const pa_pool* pool, int32_t num_seqs, int32_t q_he
   *plan = DecodePlan{};
   int32_t p = requested;
   if (p == 0) {
-    int32_t grid = 0, capacity = 0;
-    hipError_t e = pa::decode_balanced_grid(d, q_heads / d.kv_heads, num_seqs, max_context_len, &grid, &capacity);
+    pa::DecodeCapacity cap{};
+    hipError_t e = pa::decode_capacity(d, q_heads / d.kv_heads, num_seqs, max_context_len, &cap);
     if (e != hipSuccess) return hip_fail(e, "decode grid query");
     const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
-    p = units >= capacity ? static_cast<int32_t>(ceil_div(std::max(max_context_len, 1), d.block_size) * d.block_size)
-                          : 512;
+    p = units >= cap.partition
+            ? static_cast<int32_t>(ceil_div(std::max(max_context_len, 1), d.block_size) * d.block_size)
+            : 512;
   }
   if (p % d.block_size != 0)
     return fail(PA_ERR_INVALID, "partition_tokens must be a positive multiple of block_size (" +
@@ -404,7 +431,7 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
     return fail(PA_ERR_INVALID, "bad sizes");
   DecodePlan plan;
   if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
-  *resolved = plan.balanced ? PA_PARTITION_BALANCED : plan.partition_tokens;
+  *resolved = plan.balanced ? PA_PARTITION_BALANCED : plan.uniform ? PA_PARTITION_UNIFORM : plan.partition_tokens;
   return PA_OK;
 }
 
@@ -471,6 +498,7 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
   pa::DecodeArgs a = decode_args(d, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride,
                                  context_lens, max_context_len, scale);
   a.balanced = plan.balanced;
+  a.uniform = plan.uniform;
   a.grid = plan.grid;
   a.num_slots = plan.num_slots;
   a.partition_tokens = plan.partition_tokens;
@@ -482,6 +510,7 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
                      : nullptr;
     a.part_ml = reinterpret_cast<float*>(ws + plan.ml_off);
     a.part_o = reinterpret_cast<float*>(ws + plan.o_off);
+    a.unit_desc = plan.uniform ? reinterpret_cast<int32_t*>(ws + plan.desc_off) : nullptr;
   }
   hipError_t e = pa::launch_decode(d, a, st);
   return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");

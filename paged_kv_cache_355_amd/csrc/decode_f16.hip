@@ -7,9 +7,9 @@ hipError_t launch_decode_f16(const PoolDesc& p, const DecodeArgs& a, hipStream_t
   return dec::launch_dtype<kF16>(p, a, stream);
 }
 
-hipError_t decode_grid_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
-                           int32_t* partition_capacity) {
-  return dec::grid_dtype<kF16>(p, group, num_seqs, max_ctx, grid, partition_capacity);
+hipError_t decode_capacity_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx,
+                               DecodeCapacity* cap) {
+  return dec::capacity_dtype<kF16>(p, group, num_seqs, max_ctx, cap);
 }
 
 }  // namespace pa

@@ -1004,7 +1004,9 @@ __global__ __launch_bounds__(NW * 64, 3) void decode_prefix_kernel(
 //   grid = (q_heads, num_seqs, D/DC), block = kReduceThreads; one workgroup
 //   per DC output dims of a row.  With a shared prefix a row's parts are the
 //   prefix's partials followed by the suffix's; rows whose suffix is one
-//   part were finished by the partition kernel.
+//   part were finished by the partition kernel.  After the uniform split
+//   (unit_desc set) a row's records are the G-row records of its unit's
+//   tasks t0 … t0+n−1, found in unit_desc.
 //   out = Σ_p 2^(m_p − M) o_p / Σ_p 2^(m_p − M) l_p with M = max_p m_p.
 //   Each workgroup computes the per-partition weights 2^(m_p − M) into LDS
 //   (up to kReduceLds partitions; beyond that they are recomputed on the
@@ -1049,7 +1051,9 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
                                                                        const int32_t* __restrict__ seq_prefix,
                                                                        int32_t max_prefix, int32_t q_heads,
                                                                        int32_t max_parts, int32_t part_tokens,
-                                                                       int32_t max_ctx) {
+                                                                       int32_t max_ctx,
+                                                                       const int32_t* __restrict__ unit_desc,
+                                                                       int32_t group) {
   constexpr int LANES = kReduceThreads / DC;   // partition lanes per output element
   static_assert(D % DC == 0 && kReduceThreads % DC == 0, "dims split");
   const int s = blockIdx.y;
@@ -1059,25 +1063,39 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
-  const int32_t pre = prefix_of<BS>(seq_prefix, s, len_c, max_prefix);
-  const int32_t nsp = parts_of(len_c - pre, part_tokens);
-  if (nsp <= 1) return;  // finished by the partition kernel (empty, NaN and single-part rows)
-  const int32_t nparts = parts_of(pre, part_tokens) + nsp;
   const int64_t row = static_cast<int64_t>(s) * q_heads + h;
-  const float* ml = part_ml + row * max_parts * 2;
-  const float* po = part_o + row * max_parts * D;
+  // Record p of this row sits at rec0 + p·ps.
+  int32_t nparts;
+  int64_t rec0, ps;
+  if (unit_desc) {   // uniform split: the unit's records, G rows per task
+    const int64_t u = row / group;
+    nparts = unit_desc[2 * u + 1];
+    if (nparts <= 1) return;   // written by the partition's own workgroup
+    rec0 = static_cast<int64_t>(unit_desc[2 * u]) * group + h % group;
+    ps = group;
+  } else {
+    const int32_t pre = prefix_of<BS>(seq_prefix, s, len_c, max_prefix);
+    const int32_t nsp = parts_of(len_c - pre, part_tokens);
+    if (nsp <= 1) return;  // finished by the partition kernel (empty, NaN and single-part rows)
+    nparts = parts_of(pre, part_tokens) + nsp;
+    rec0 = row * max_parts;
+    ps = 1;
+  }
+  const float* ml = part_ml + rec0 * 2;
+  const float* po = part_o + rec0 * D;
+  const int64_t mls = 2 * ps, pos = ps * D;
 
   __shared__ float sh_red[kReduceThreads / 64];
   __shared__ float sh_w[kReduceLds];
   __shared__ float sh_acc[LANES][DC];
   float mm = kNegBig;
-  for (int p = tid; p < nparts; p += kReduceThreads) mm = fmaxf(mm, ml[2 * p]);
+  for (int p = tid; p < nparts; p += kReduceThreads) mm = fmaxf(mm, ml[p * mls]);
   const float M = block_reduce_max(mm, sh_red);
   float part = 0.f;
   for (int p = tid; p < nparts; p += kReduceThreads) {
-    const float wgt = exp2f_fast(ml[2 * p] - M);
+    const float wgt = exp2f_fast(ml[p * mls] - M);
     if (p < kReduceLds) sh_w[p] = wgt;
-    part += ml[2 * p + 1] * wgt;   // a NaN sum marks a partition that met a bad block id
+    part += ml[p * mls + 1] * wgt;   // a NaN sum marks a partition that met a bad block id
   }
   const float L = block_reduce_sum(part, sh_red);   // its barriers also publish sh_w
   const int dl = tid % DC;
@@ -1090,13 +1108,13 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int pp = p + k * LANES;
-      const float wgt = pp < kReduceLds ? sh_w[pp] : exp2f_fast(ml[2 * pp] - M);
-      acc[k] = __builtin_fmaf(wgt, po[static_cast<int64_t>(pp) * D + d], acc[k]);
+      const float wgt = pp < kReduceLds ? sh_w[pp] : exp2f_fast(ml[pp * mls] - M);
+      acc[k] = __builtin_fmaf(wgt, po[pp * pos + d], acc[k]);
     }
   }
   for (; p < nparts; p += LANES) {
-    const float wgt = p < kReduceLds ? sh_w[p] : exp2f_fast(ml[2 * p] - M);
-    acc[0] = __builtin_fmaf(wgt, po[static_cast<int64_t>(p) * D + d], acc[0]);
+    const float wgt = p < kReduceLds ? sh_w[p] : exp2f_fast(ml[p * mls] - M);
+    acc[0] = __builtin_fmaf(wgt, po[p * pos + d], acc[0]);
   }
   sh_acc[pl][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
@@ -1403,27 +1421,203 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
 }
 
 // ---------------------------------------------------------------------------
+// Uniform split: every (sequence, kv-head) unit is cut into partitions of one
+// length P, chosen on the device from the lengths so that all of the batch's
+// partitions fit in one grid of `budget` workgroups that are resident at
+// once.  Tasks are numbered densely, so workgroup t (on XCD t mod 8) always
+// has work and each XCD gets an equal count, with no idle workgroups mixed
+// in.
+// ---------------------------------------------------------------------------
+constexpr int kUniformLaneLens = 4;   // lengths a lane keeps in registers (the batch's first 256)
+
+// A length as the split counts it: a valid length as it is, an empty or
+// invalid one as 0 (its unit still takes one workgroup, which writes its zero
+// or NaN rows), -1 past the end of the batch.
+__device__ __forceinline__ int32_t split_len(const int32_t* __restrict__ lens, int32_t s, int32_t num_seqs,
+                                             int32_t max_ctx) {
+  if (s >= num_seqs) return -1;
+  const int32_t l = lens[s];
+  return (l < 0 || l > max_ctx) ? 0 : l;
+}
+
+// Partitions of P tokens that a unit of split length l takes.
+__device__ __forceinline__ int64_t unit_parts(int32_t l, int64_t P) {
+  return l < 0 ? 0 : (l == 0 ? 1 : (l + P - 1) / P);
+}
+
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+struct UniformTask {
+  int32_t s, g, p;   // sequence, kv-head, partition
+  int32_t n;         // partitions of this unit
+  int32_t t0;        // task index of its partition 0
+  int64_t P;         // partition length in tokens
+};
+
+// Task t of the uniform split.  Every wave computes it on its own (registers
+// and cross-lane operations only).  Returns false past the last task.
+template <int BS>
+__device__ bool uniform_task(const int32_t* __restrict__ lens, int32_t num_seqs, int32_t kv_heads, int32_t max_ctx,
+                             int64_t t, int64_t budget, UniformTask* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t kmax = max<int64_t>(1, (static_cast<int64_t>(max_ctx) + BS - 1) / BS);
+  const int64_t per_head = budget / kv_heads;   // partitions one kv-head may take over the whole batch
+  if (per_head <= num_seqs) {                   // no room to split: one workgroup per unit
+    if (t >= static_cast<int64_t>(num_seqs) * kv_heads) return false;
+    out->s = static_cast<int32_t>(t / kv_heads);
+    out->g = static_cast<int32_t>(t % kv_heads);
+    out->p = 0;
+    out->n = 1;
+    out->t0 = static_cast<int32_t>(t);
+    out->P = kmax * BS;
+    return true;
+  }
+  constexpr int kCached = 64 * kUniformLaneLens;
+  int32_t lc[kUniformLaneLens];
+  int64_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kUniformLaneLens; ++k) {
+    lc[k] = split_len(lens, 64 * k + lane, num_seqs, max_ctx);
+    sum += max(lc[k], 0);
+  }
+  for (int32_t s = kCached + lane; s < num_seqs; s += 64) sum += max(split_len(lens, s, num_seqs, max_ctx), 0);
+  sum = uniform(wave_sum(sum));
+  auto count = [&](int64_t P) -> int64_t {
+    int64_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kUniformLaneLens; ++k) c += unit_parts(lc[k], P);
+    for (int32_t s = kCached + lane; s < num_seqs; s += 64) c += unit_parts(split_len(lens, s, num_seqs, max_ctx), P);
+    return uniform(wave_sum(c));
+  };
+  // Smallest k with count(k·BS) ≤ per_head.  Σ⌈l/P⌉ ≥ Σl/P bounds k from
+  // below; Σ⌈l/P⌉ ≤ Σl/P + num_seqs gives a k that fits; kmax (one partition
+  // per unit) always fits.
+  int64_t lo = max<int64_t>(1, (sum + per_head * BS - 1) / (per_head * BS));
+  const int64_t room = (per_head - num_seqs) * BS;
+  int64_t hi = max(lo, min(kmax, (sum + room - 1) / room));
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (count(mid * BS) <= per_head) hi = mid;
+    else lo = mid + 1;
+  }
+  const int64_t P = hi * BS;
+  // Tasks in batch order: sequence s holds kv_heads × n_s consecutive tasks,
+  // kv-head by kv-head.  Scan 64 sequences at a time for the one holding t.
+  int64_t base = 0;
+  auto visit = [&](int32_t l, int32_t s0) -> bool {
+    const int64_t n = unit_parts(l, P);
+    const int64_t c = n * kv_heads;
+    int64_t incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int64_t total = uniform(__shfl(incl, 63, 64));
+    if (t >= base + total) {
+      base += total;
+      return false;
+    }
+    const int w = __builtin_ctzll(__ballot(base + incl > t));
+    const int64_t before = uniform(__shfl(incl - c, w, 64));
+    const int64_t nn = uniform(__shfl(n, w, 64));
+    const int64_t local = t - base - before;
+    out->s = s0 + w;
+    out->g = static_cast<int32_t>(local / nn);
+    out->p = static_cast<int32_t>(local % nn);
+    out->n = static_cast<int32_t>(nn);
+    out->t0 = static_cast<int32_t>(t - out->p);
+    out->P = P;
+    return true;
+  };
+#pragma unroll
+  for (int k = 0; k < kUniformLaneLens; ++k)
+    if (visit(lc[k], 64 * k)) return true;
+  for (int32_t s0 = kCached; s0 < num_seqs; s0 += 64)
+    if (visit(split_len(lens, s0 + lane, num_seqs, max_ctx), s0)) return true;
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// decode_uniform_kernel
+//   grid = budget workgroups (1-D, all resident at once), block = NW × 64.
+//   Workgroup t runs task t of uniform_task: tokens [p·P, min((p+1)·P, len))
+//   of unit (s, g).  A unit of one partition writes its output rows; a unit
+//   of n > 1 writes one record per partition at its task index (rows
+//   t·G … t·G+G−1) and, from partition 0, (t0, n) into unit_desc[unit] for
+//   decode_reduce_kernel.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void decode_uniform_kernel(
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
+    void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
+    int32_t* __restrict__ unit_desc, const int32_t* __restrict__ block_tables, int32_t table_stride,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_blocks, int32_t kv_heads,
+    int32_t max_ctx, float scale_log2) {
+  const int64_t t = blockIdx.x;
+  UniformTask tk;
+  if (!uniform_task<BS>(context_lens, num_seqs, kv_heads, max_ctx, t, gridDim.x, &tk)) return;
+  const int32_t s = tk.s, g = tk.g;
+  const int q_heads = kv_heads * G;
+  if (tk.p == 0 && threadIdx.x == 0) {
+    const int64_t u = static_cast<int64_t>(s) * kv_heads + g;
+    unit_desc[2 * u] = tk.t0;
+    unit_desc[2 * u + 1] = tk.n;
+  }
+  const int32_t len = context_lens[s];
+  const bool bad_len = len < 0 || len > max_ctx;
+  if (bad_len || len == 0) {
+    fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
+    return;
+  }
+  const int32_t t_begin = static_cast<int32_t>(tk.p * tk.P);
+  const int32_t t_end = static_cast<int32_t>(min<int64_t>(t_begin + tk.P, len));
+  const bool single = tk.n == 1;
+  const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
+  __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
+  const bool shared = shares_first_block(block_tables, table_stride, s, num_seqs);
+  attend_range_policy<DT, D, BS, G, NW>(
+      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
+      [&](int r, int d, float M, float L, float O, bool bad) {
+        if (single) {
+          const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
+          store_out(out, out_dtype, row * D + d, bad ? qnan() : (L > 0.f ? O / L : (L != L ? qnan() : 0.f)));
+          return;
+        }
+        const int64_t rec = t * G + r;
+        part_o[rec * D + d] = bad ? qnan() : O;
+        if (d == 0) {
+          part_ml[2 * rec] = M;
+          part_ml[2 * rec + 1] = L;
+        }
+      });
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch
 // ---------------------------------------------------------------------------
 
-// Workgroups of the fixed-partition kernel that fit on the current device at once.
-template <int DT, int D, int BS, int G>
-hipError_t partition_resident(int32_t* resident_out) {
+// Workgroups of `kernel` (kThreads threads, static LDS only) that the current
+// device holds at once; cached per device in `cache`.
+template <typename Kernel>
+hipError_t resident_workgroups(Kernel kernel, int (&cache)[64], int32_t* resident_out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  static int cached[64];
-  int resident = dev >= 0 && dev < 64 ? cached[dev] : 0;
+  int resident = dev >= 0 && dev < 64 ? cache[dev] : 0;
   if (resident == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partition_kernel<DT, D, BS, G, kWaves>,
-                                                     kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     resident = per_cu * cus;
     if (resident <= 0) resident = cus > 0 ? cus : 1;
-    if (dev >= 0 && dev < 64) cached[dev] = resident;
+    if (dev >= 0 && dev < 64) cache[dev] = resident;
   }
   *resident_out = resident;
   return hipSuccess;
@@ -1434,22 +1628,10 @@ hipError_t partition_resident(int32_t* resident_out) {
 template <int DT, int D, int BS, int G>
 hipError_t balanced_grid(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
   constexpr int CT = Chunk<DT, D, BS>::CT;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  static int cache[64];
+  int32_t resident = 0;
+  hipError_t e = resident_workgroups(decode_balanced_kernel<DT, D, BS, G, kWaves>, cache, &resident);
   if (e != hipSuccess) return e;
-  static int cached[64];   // resident workgroups per device, 0 = not yet asked
-  int resident = dev >= 0 && dev < 64 ? cached[dev] : 0;
-  if (resident == 0) {
-    int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_balanced_kernel<DT, D, BS, G, kWaves>, kThreads,
-                                                     0);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    resident = per_cu * cus;
-    if (resident <= 0) resident = cus > 0 ? cus : 1;
-    if (dev >= 0 && dev < 64) cached[dev] = resident;
-  }
   int64_t W = resident;
   if (const char* v = std::getenv("PA_DECODE_GRID")) {
     const long x = std::strtol(v, nullptr, 10);
@@ -1463,6 +1645,21 @@ hipError_t balanced_grid(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, i
   return hipSuccess;
 }
 
+// The merge of partial records; fewer rows than CUs split each row's dims
+// over D/16 workgroups.
+template <int D, int BS, int G>
+void launch_reduce(const DecodeArgs& a, const int32_t* seq_prefix, const int32_t* unit_desc, hipStream_t stream) {
+  if (static_cast<int64_t>(a.q_heads) * a.num_seqs < kReduceSplitRows) {
+    hipLaunchKernelGGL((decode_reduce_kernel<D, 16, BS>), dim3(a.q_heads, a.num_seqs, D / 16), dim3(kReduceThreads),
+                       0, stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, seq_prefix, a.max_prefix,
+                       a.q_heads, a.max_parts, a.partition_tokens, a.max_context_len, unit_desc, G);
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<D, D, BS>), dim3(a.q_heads, a.num_seqs, 1), dim3(kReduceThreads), 0,
+                       stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, seq_prefix, a.max_prefix,
+                       a.q_heads, a.max_parts, a.partition_tokens, a.max_context_len, unit_desc, G);
+  }
+}
+
 template <int DT, int D, int BS, int G>
 hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
   if (a.balanced) {
@@ -1471,6 +1668,17 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
                        a.out, a.out_dtype, a.counters, a.part_ml, a.part_o, a.block_tables, a.table_stride,
                        a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.num_slots,
                        a.scale_log2);
+    return hipGetLastError();
+  }
+  if (a.uniform) {
+    hipLaunchKernelGGL((decode_uniform_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
+                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
+                       a.out, a.out_dtype, a.part_ml, a.part_o, a.unit_desc, a.block_tables, a.table_stride,
+                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.scale_log2);
+    hipError_t e = hipGetLastError();
+    // with no more than one workgroup per unit and kv-head nothing splits (uniform_task)
+    if (e != hipSuccess || a.grid / p.kv_heads <= a.num_seqs) return e;
+    launch_reduce<D, BS, G>(a, nullptr, a.unit_desc, stream);
     return hipGetLastError();
   }
   const bool shared_prefix = a.group_start != nullptr && a.num_groups > 0 && a.max_prefix > 0;
@@ -1503,16 +1711,7 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
                      a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || suffix_parts <= 1) return e;
-  // fewer rows than CUs: split each row's dims over D/16 workgroups
-  if (static_cast<int64_t>(a.q_heads) * a.num_seqs < kReduceSplitRows) {
-    hipLaunchKernelGGL((decode_reduce_kernel<D, 16, BS>), dim3(a.q_heads, a.num_seqs, D / 16), dim3(kReduceThreads),
-                       0, stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, seq_prefix, a.max_prefix,
-                       a.q_heads, a.max_parts, a.partition_tokens, a.max_context_len);
-  } else {
-    hipLaunchKernelGGL((decode_reduce_kernel<D, D, BS>), dim3(a.q_heads, a.num_seqs, 1), dim3(kReduceThreads), 0,
-                       stream, a.out, a.out_dtype, a.part_ml, a.part_o, a.context_lens, seq_prefix, a.max_prefix,
-                       a.q_heads, a.max_parts, a.partition_tokens, a.max_context_len);
-  }
+  launch_reduce<D, BS, G>(a, seq_prefix, nullptr, stream);
   return hipGetLastError();
 }
 
@@ -1555,12 +1754,14 @@ struct LaunchFn {
 };
 
 template <int DT, int D, int BS, int G>
-struct GridFn {
-  static hipError_t run(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
-                        int32_t* partition_capacity) {
-    hipError_t e = balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, grid);
+struct CapacityFn {
+  static hipError_t run(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, DecodeCapacity* cap) {
+    static int partition_cache[64], uniform_cache[64];
+    hipError_t e = balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, &cap->balanced_grid);
     if (e != hipSuccess) return e;
-    return partition_resident<DT, D, BS, G>(partition_capacity);
+    e = resident_workgroups(decode_partition_kernel<DT, D, BS, G, kWaves>, partition_cache, &cap->partition);
+    if (e != hipSuccess) return e;
+    return resident_workgroups(decode_uniform_kernel<DT, D, BS, G, kWaves>, uniform_cache, &cap->uniform);
   }
 };
 
@@ -1570,9 +1771,8 @@ hipError_t launch_dtype(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
 }
 
 template <int DT>
-hipError_t grid_dtype(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
-                      int32_t* partition_capacity) {
-  return dispatch<DT, GridFn>(p, group, num_seqs, max_ctx, grid, partition_capacity);
+hipError_t capacity_dtype(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, DecodeCapacity* cap) {
+  return dispatch<DT, CapacityFn>(p, group, num_seqs, max_ctx, cap);
 }
 
 }  // namespace dec

@@ -147,12 +147,12 @@ hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t str
   }
 }
 
-hipError_t decode_balanced_grid(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
-                                int32_t* grid, int32_t* partition_capacity) {
+hipError_t decode_capacity(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
+                           DecodeCapacity* cap) {
   switch (p.dtype) {
-    case kF32: return decode_grid_f32(p, group, num_seqs, max_context_len, grid, partition_capacity);
-    case kF16: return decode_grid_f16(p, group, num_seqs, max_context_len, grid, partition_capacity);
-    case kBF16: return decode_grid_bf16(p, group, num_seqs, max_context_len, grid, partition_capacity);
+    case kF32: return decode_capacity_f32(p, group, num_seqs, max_context_len, cap);
+    case kF16: return decode_capacity_f16(p, group, num_seqs, max_context_len, cap);
+    case kBF16: return decode_capacity_bf16(p, group, num_seqs, max_context_len, cap);
     default: return hipErrorInvalidValue;
   }
 }

@@ -41,11 +41,17 @@ struct DecodeArgs {
   int32_t grid;
   int32_t num_slots;       // num_seqs * kv_heads + grid
   int32_t* counters;       // [kMergeLevels][num_slots], zero on entry and exit
-  // Fixed partitions (balanced = false).
+  // Uniform split (uniform = true): `grid` workgroups, all resident at once;
+  // the device picks one partition length that fits the batch's partitions
+  // into them.  Partial records: [grid][group] rows; unit_desc[num_seqs ×
+  // kv_heads][2] = (first task, partitions) of every unit.
+  bool uniform = false;
+  int32_t* unit_desc = nullptr;
+  // Fixed partitions (balanced = false, uniform = false).
   int32_t partition_tokens;
   int32_t max_parts;       // partitions covering max_context_len
   // Partial records.  Fixed partitions: [num_seqs][q_heads][max_parts] rows;
-  // balanced: [num_slots][group] rows.
+  // balanced: [num_slots][group] rows; uniform: [grid][group] rows.
   float* part_ml;          // rows × (max, sum)
   float* part_o;           // rows × head_dim
   // Shared prefixes (fixed partitions only; all null/0 for plain decode):
@@ -76,21 +82,24 @@ hipError_t launch_swap_blocks(const PoolDesc& p, const int32_t* blocks, int32_t 
                               hipStream_t stream);
 hipError_t launch_decode(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 
-// Workgroups of the balanced decode kernel for these sizes (every one
-// resident on the current device at once; PA_DECODE_GRID overrides), and the
-// number of fixed-partition workgroups the device holds at once.
-hipError_t decode_balanced_grid(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
-                                int32_t* grid, int32_t* partition_capacity);
+// Workgroups the current device holds at once, per decode kernel.
+struct DecodeCapacity {
+  int32_t balanced_grid;   // the balanced kernel's grid for these sizes (PA_DECODE_GRID overrides)
+  int32_t partition;       // fixed-partition workgroups resident at once
+  int32_t uniform;         // uniform-split workgroups resident at once
+};
+hipError_t decode_capacity(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_context_len,
+                           DecodeCapacity* cap);
 
 // Per-dtype decode launchers and grid queries (decode_<dtype>.hip).
 hipError_t launch_decode_f32(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream);
-hipError_t decode_grid_f32(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
-                           int32_t* partition_capacity);
-hipError_t decode_grid_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
-                           int32_t* partition_capacity);
-hipError_t decode_grid_bf16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx, int32_t* grid,
-                           int32_t* partition_capacity);
+hipError_t decode_capacity_f32(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx,
+                               DecodeCapacity* cap);
+hipError_t decode_capacity_f16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx,
+                               DecodeCapacity* cap);
+hipError_t decode_capacity_bf16(const PoolDesc& p, int32_t group, int32_t num_seqs, int32_t max_ctx,
+                               DecodeCapacity* cap);
 
 }  // namespace pa

@@ -126,7 +126,9 @@ def test_decode_matches_oracle(gpu, dtype, head_dim, block_size, group):
     seed = zlib.crc32(repr((dtype, head_dim, block_size, group)).encode())
     case = build_case(lens, kv_heads, group, head_dim, block_size, dtype, seed, scale=1.0)
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], dtype)
-    for partition in (2 * block_size, 0):                 # many partitions + reduce; one partition
+    # fixed partitions + reduce; the automatic choice for a batch this small (the
+    # uniform split); the balanced split
+    for partition in (2 * block_size, 0, pk.PA_PARTITION_BALANCED):
         got = out_to_f64(run_decode(pk, case, kv_heads, head_dim, block_size, dtype, out_dtype="f32",
                                     partition_tokens=partition))
         assert np.all(np.isfinite(got))
@@ -206,7 +208,7 @@ def test_decode_shared_prefix_matches_private_copy(gpu):
     # fixed partitions: the summation order depends only on logical positions → identical bits
     got = run_decode(pk, case, hkv, d, bs, "f16", out_dtype="f32", partition_tokens=32).cpu()
     assert (got[0] == got[1]).all() and (got[0] == got[2]).all()
-    # balanced split: each sequence may be cut at other places, so equal up to fp32 rounding
+    # the automatic split (uniform for three units): cuts depend on the lengths only, but allow fp32 rounding
     got = out_to_f64(run_decode(pk, case, hkv, d, bs, "f16", out_dtype="f32"))
     assert np.max(np.abs(got[0] - got[1])) <= 1e-6 and np.max(np.abs(got[0] - got[2])) <= 1e-6
 
@@ -229,6 +231,47 @@ def test_balanced_split_any_grid(gpu, grid):
         del os.environ["PA_DECODE_GRID"]
     assert np.all(got[1] == 0.0)
     assert np.max(np.abs(got - want)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("grid", [1, 6, 7, 37, 4000])
+def test_uniform_split_any_grid(gpu, grid):
+    """The uniform split for any grid: at most one workgroup per unit (no
+    split, no reduce), one spare workgroup, a few, and more workgroups than
+    blocks, which cuts the longest sequence into ~150 one-block partitions."""
+    pk = gpu
+    lens = [4999, 0, 3, 700, 31, 1]
+    case = build_case(lens, 1, 8, 128, 32, "bf16", 98, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "bf16")
+    os.environ["PA_DECODE_GRID"] = str(grid)
+    try:
+        got = out_to_f64(run_decode(pk, case, 1, 128, 32, "bf16", out_dtype="f32",
+                                    partition_tokens=pk.PA_PARTITION_UNIFORM))
+    finally:
+        del os.environ["PA_DECODE_GRID"]
+    assert np.all(got[1] == 0.0)
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
+
+
+def test_uniform_split_workspace_needs_no_fill(gpu):
+    """The uniform split writes every record and unit descriptor it reads:
+    a workspace of 0xFF bytes serves it, also again for a smaller batch
+    (whose descriptors then overlap the larger call's)."""
+    import torch
+    pk = gpu
+    case = build_case([900, 17, 2500, 64, 0, 333], 2, 4, 64, 16, "f16", 6, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
+    pool = pk.Pool(case["num_blocks"], 16, 2, 64, "f16", k=to_torch(case["k_pool"], "f16"),
+                   v=to_torch(case["v_pool"], "f16"))
+    q, tables, lens = to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(), \
+        torch.from_numpy(case["lens"]).cuda()
+    uni = pk.PA_PARTITION_UNIFORM
+    assert pk.decode_partition_tokens(pool, 6, 8, 2500, 0) == uni       # the automatic choice here
+    ws = torch.full((pk.decode_workspace_bytes(pool, 6, 8, 2500, uni),), 255, dtype=torch.uint8, device="cuda")
+    for n in (6, 3, 6):
+        out = pk.decode(pool, q[:n].contiguous(), tables[:n].contiguous(), lens[:n].contiguous(), 2500,
+                        out_dtype="f32", workspace=ws, partition_tokens=uni)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(out_to_f64(out) - want[:n])) <= TOL["f16"]
 
 
 def test_balanced_workspace_reuse_leaves_counters_zero(gpu):
@@ -271,18 +314,20 @@ def test_whole_sequence_batch_order(gpu, n_seqs):
     """One workgroup per (sequence, kv-head) with a partition longer than any
     sequence; workgroups start in batch order.  Every row matches the oracle,
     and reversing the batch reverses the rows bit for bit (a unit's result
-    does not depend on when or where it runs).  Many equal lengths."""
+    does not depend on when or where it runs).  Many equal lengths.  The
+    uniform split on the same batch (300 sequences: lengths past the 256 a
+    wave keeps in registers) reverses bit for bit too."""
     pk = gpu
     rng = np.random.default_rng(n_seqs)
     lens = [int(x) for x in rng.choice([0, 1, 17, 64, 200], size=n_seqs)]
     case = build_case(lens, 2, 2, 64, 16, "f16", n_seqs, scale=1.0)
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
     rev = dict(case, q=case["q"][::-1].copy(), tables=case["tables"][::-1].copy(), lens=case["lens"][::-1].copy())
-    for partition in (208, pk.PA_PARTITION_BALANCED):
+    for partition in (208, pk.PA_PARTITION_UNIFORM, pk.PA_PARTITION_BALANCED):
         got = out_to_f64(run_decode(pk, case, 2, 64, 16, "f16", out_dtype="f32", partition_tokens=partition))
         assert np.max(np.abs(got - want)) <= TOL["f16"], partition
         got_rev = out_to_f64(run_decode(pk, rev, 2, 64, 16, "f16", out_dtype="f32", partition_tokens=partition))
-        if partition == 208:
+        if partition != pk.PA_PARTITION_BALANCED:   # the uniform length depends only on the multiset of lengths
             assert np.array_equal(got_rev, got[::-1])
         else:
             assert np.max(np.abs(got_rev[::-1] - want)) <= TOL["f16"]
@@ -305,11 +350,12 @@ def test_decode_rejects_bad_metadata_under_validation(gpu):
                   torch.from_numpy(case["lens"]).cuda(), 10)         # a length above max_context_len
 
 
-@pytest.mark.parametrize("partition", [8, 0])
+@pytest.mark.parametrize("partition", [8, -1, -2])
 def test_decode_bad_table_entry_gives_nan_not_a_fault(gpu, partition):
     """With host validation off, the kernel's own bounds check turns a block id
-    outside the pool into NaN output for that sequence only (fixed partitions
-    and the balanced split, whose pieces carry the mark through the merge)."""
+    outside the pool into NaN output for that sequence only (fixed partitions,
+    the balanced split, whose pieces carry the mark through the merge, and the
+    uniform split, whose records carry it through the reduce)."""
     pk = gpu
     case = build_case([20, 9, 30], 1, 1, 64, 4, "f16", 4)
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
@@ -344,7 +390,7 @@ def test_decode_empty_batch_and_argument_errors(gpu):
                   torch.ones((1,), dtype=torch.int32, device="cuda"), 1, partition_tokens=24)
 
 
-@pytest.mark.parametrize("partition", [0, -1, 4])
+@pytest.mark.parametrize("partition", [0, -1, -2, 4])
 def test_decode_maximum_batch(gpu, partition):
     """65535 sequences (the largest batch the ABI takes: one grid dimension)
     of 0-9 tokens, in every split mode; sampled rows against the oracle,

@@ -188,10 +188,11 @@ def test_gqa70b_bf16_full(gpu):
     run_step(gpu, "gqa70b_bf16")
 
 
-@pytest.mark.parametrize("partition", [512, -1])
+@pytest.mark.parametrize("partition", [512, -1, -2])
 def test_gqa70b_bf16_split_full(gpu, partition):
     """The GQA batch split into 512-token partitions (16384 rows for the
-    reduce kernel, one workgroup per row) and by the balanced split."""
+    reduce kernel, one workgroup per row), by the balanced split and by the
+    uniform split (2048 units: one workgroup each, no reduce)."""
     run_step(gpu, "gqa70b_bf16", partition_tokens=partition)
 
 
@@ -214,5 +215,8 @@ def test_prefix_share_shared_prefix_decode_full(gpu, cow_step):
     assert len(r["pairs"]) == (224 if cow_step else 0)
 
 
-def test_long_splitk_bf16_full(gpu):
-    run_step(gpu, "long_splitk_bf16", samples=3)
+@pytest.mark.parametrize("partition", [None, -2])
+def test_long_splitk_bf16_full(gpu, partition):
+    """The long-context batch with the workload's 512-token partitions and
+    with the uniform split (~1100-token partitions, one resident grid)."""
+    run_step(gpu, "long_splitk_bf16", samples=3, partition_tokens=partition)
