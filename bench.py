@@ -57,7 +57,8 @@ def parse_args():
                     help="a smaller batch of the workload's sequences (default: the workload's own batch)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0 = the workload's setting (the library's automatic choice unless it names fixed "
-                         "partitions); -1 = the balanced split; > 0 = fixed partitions of that many tokens")
+                         "partitions); -1 = the balanced split; -2 = the uniform split; > 0 = fixed partitions of "
+                         "that many tokens")
     ap.add_argument("--decode", choices=["auto", "plain", "shared"], default="auto",
                     help="auto = pa_decode_shared_prefix when the batch has prefix groups, else pa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -534,7 +535,9 @@ def main():
         "roofline": {
             "kernel": ("pa_decode_shared_prefix: decode_prefix_kernel + decode_partition_kernel" +
                        (" + decode_reduce_kernel" if resolved_part < max_ctx_bound else "") if shared_prefix else
-                       "pa_decode: decode_balanced_kernel" if resolved_part < 0 else
+                       "pa_decode: decode_balanced_kernel" if resolved_part == -1 else
+                       "pa_decode: decode_uniform_kernel + decode_reduce_kernel (uniform split)"
+                       if resolved_part == -2 else
                        "pa_decode: decode_partition_kernel" + (" + decode_reduce_kernel"
                                                                if resolved_part < max_ctx_bound else
                                                                " (one workgroup per sequence and kv-head)")),

@@ -28,11 +28,16 @@
 //     (two register buffers).
 //   * Softmax runs in base 2: scores carry scale·log2(e) and v_exp_f32 does 2^x.
 //
-// Three ways of dealing out the work (all exact up to fp32 rounding order):
+// Four ways of dealing out the work (all exact up to fp32 rounding order):
 //   * Whole sequences: one workgroup per (sequence, kv-head), started in
 //     batch order; the automatic choice when the batch has at least as many
 //     units as the device holds workgroups at once.
-//   * Balanced (the automatic choice for smaller batches): the (sequence,
+//   * Uniform (the automatic choice for smaller batches): one fully resident
+//     grid; every workgroup derives from the lengths the shortest partition
+//     length whose partitions of all units fit the grid, numbers the
+//     partitions densely and runs one; decode_reduce_kernel merges units of
+//     more than one partition.
+//   * Balanced (on request): the (sequence,
 //     kv-head) units are laid end to end on one axis of CT-token chunks and
 //     every workgroup of a single, fully resident grid takes an equal slice
 //     of that axis.  Units cut by a slice boundary produce partial (max, sum,
