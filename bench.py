@@ -18,7 +18,9 @@ the workload's shape, resident in HBM before timing starts.
 
 Printed: one JSON line.  ``value`` is KV bytes read by decode per second of
 the whole timed region (host step, copies and kernels included);
-``roofline`` is the decode call alone, timed with HIP events on its stream;
+``roofline`` is the decode call alone, timed with HIP events on its stream
+around the first layer's call of every timed step (``--timed-layers all``
+brackets every layer's; each event pair costs the step about 5 us);
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
@@ -61,6 +63,12 @@ def parse_args():
                          "that many tokens")
     ap.add_argument("--decode", choices=["auto", "plain", "shared"], default="auto",
                     help="auto = pa_decode_shared_prefix when the batch has prefix groups, else pa_decode")
+    ap.add_argument("--timed-layers", choices=["first", "all"], default="first",
+                    help="decode calls bracketed by HIP events: the first layer's of every step (default) "
+                         "or every layer's")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="one pa_decode_append call per layer (KV write inside the decode launch) instead of "
+                         "pa_write_kv then pa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-admission (bulk pa_write_kv) probe")
     ap.add_argument("--no-swap", action="store_true", help="skip the block swap (pa_swap_out / pa_swap_in) probe")
@@ -141,9 +149,11 @@ def split_meta(flat, B, stride):
 # ----------------------------------------------------------------------------
 # the timed step
 # ----------------------------------------------------------------------------
-def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, shared_prefix):
+def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, shared_prefix, fused_append):
     """n_steps decode steps; returns per-step KV bytes read by decode.  With
-    shared_prefix the batch's prefix groups go to pa_decode_shared_prefix."""
+    shared_prefix the batch's prefix groups go to pa_decode_shared_prefix;
+    with fused_append each layer's KV write and decode are one
+    pa_decode_append call, else pa_write_kv then pa_decode."""
     import numpy as np
     import torch
     from paged_kv_cache_355_amd._lib import lib, check
@@ -179,9 +189,12 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
         for layer, pool in enumerate(st["pools"]):
             if n_cow:
                 check(L.pa_copy_blocks(pool.handle, dev["pairs"].data_ptr(), n_cow, sptr), "pa_copy_blocks")
-            check(L.pa_write_kv(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
-                                dev["slots"].data_ptr(), B, sptr), "pa_write_kv")
-            if timing is not None:
+            fused = fused_append and not shared_prefix
+            if not fused:
+                check(L.pa_write_kv(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
+                                    dev["slots"].data_ptr(), B, sptr), "pa_write_kv")
+            timed = timing is not None and (timing["all_layers"] or layer == 0)
+            if timed:
                 ev0, ev1 = timing["free"].pop()
                 ev0.record(stream)
             if shared_prefix:
@@ -190,12 +203,18 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
                     B, w.q_heads, dev["tables"].data_ptr(), stride, dev["lens"].data_ptr(), max_len, 0.0, n_groups,
                     dev["group_start"].data_ptr(), dev["prefix"].data_ptr(), max_group, max_prefix, partition_tokens,
                     ws.data_ptr(), ws_bytes, sptr), "pa_decode_shared_prefix")
+            elif fused:   # the new token's KV write runs inside the decode launch
+                check(L.pa_decode_append(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
+                                         dev["slots"].data_ptr(), st["out"][layer].data_ptr(),
+                                         pk.api.DTYPE_CODES[w.dtype], st["q"][layer].data_ptr(), B, w.q_heads,
+                                         dev["tables"].data_ptr(), stride, dev["lens"].data_ptr(), max_len, 0.0,
+                                         partition_tokens, ws.data_ptr(), ws_bytes, sptr), "pa_decode_append")
             else:
                 check(L.pa_decode(pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype],
                                   st["q"][layer].data_ptr(), B, w.q_heads, dev["tables"].data_ptr(), stride,
                                   dev["lens"].data_ptr(), max_len, 0.0, partition_tokens, ws.data_ptr(), ws_bytes,
                                   sptr), "pa_decode")
-            if timing is not None:
+            if timed:
                 ev1.record(stream)
                 timing["used"].append((ev0, ev1))
         # logical bytes (every sequence's tokens) and unique bytes (each filled slot once:
@@ -479,14 +498,18 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] state ready; warmup {args.warmup} steps")
 
-    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None, shared_prefix)
+    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None, shared_prefix, args.fused_append)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    timing = {"used": [], "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                                   for _ in range(args.steps * args.layers)]}
+    # HIP events around the decode call of the first layer of every step (or of
+    # every layer): each recorded pair adds about 5 us of GPU time to a step
+    timing = {"used": [], "all_layers": args.timed_layers == "all",
+              "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps * args.layers)]}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    kv_bytes = run_steps(pk, w, st, args.steps, part, dev, hbufs, args.warmup, timing, shared_prefix)
+    kv_bytes = run_steps(pk, w, st, args.steps, part, dev, hbufs, args.warmup, timing, shared_prefix,
+                         args.fused_append)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     dec_ms = [a.elapsed_time(b) for a, b in timing["used"]]
@@ -494,12 +517,15 @@ def main():
 
     total_kv = sum(b for b, _ in kv_bytes)
     total_unique = sum(u for _, u in kv_bytes)
-    per_call_bytes = total_unique / len(dec_ms)   # the minimum traffic: shared blocks once
+    layers = len(st["pools"])
+    # every layer's decode reads the same tokens (same tables and lengths);
+    # the minimum traffic counts shared blocks once
+    per_call_bytes = total_unique / (args.steps * layers)
     mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = per_call_bytes / mean_dec_s / 1e9
     value = total_kv / elapsed / 1e9
-    layers = len(st["pools"])
-    traffic, traffic_ratio = recorded_traffic(w.name, "pa_decode_shared_prefix" if shared_prefix else "pa_decode")
+    entry = "pa_decode_shared_prefix" if shared_prefix else ("pa_decode_append" if args.fused_append else "pa_decode")
+    traffic, traffic_ratio = recorded_traffic(w.name, entry)
     dec_sorted = sorted(dec_ms)
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seq-steps/s, 7B shape",
@@ -518,7 +544,7 @@ def main():
             "workload": w.name, "batch": B, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "pool_blocks": sc.num_blocks,
             "layers_per_step": layers, "partition_tokens": resolved_part,
-            "decode": "pa_decode_shared_prefix" if shared_prefix else "pa_decode",
+            "decode": entry,
             "context_lens": "uniform [128, 2048] before the first warmup step, +1 per step"
             if w.name == "mha7b_fp16" else w.notes,
             "mean_context_len_timed": round(total_kv / (args.steps * layers * 2 * w.kv_heads * w.head_dim *
@@ -535,10 +561,11 @@ def main():
         "roofline": {
             "kernel": ("pa_decode_shared_prefix: decode_prefix_kernel + decode_partition_kernel" +
                        (" + decode_reduce_kernel" if resolved_part < max_ctx_bound else "") if shared_prefix else
-                       "pa_decode: decode_balanced_kernel" if resolved_part == -1 else
-                       "pa_decode: decode_uniform_kernel + decode_reduce_kernel (uniform split)"
+                       entry + (": write_kv_kernel + decode_balanced_kernel" if entry == "pa_decode_append"
+                                else ": decode_balanced_kernel") if resolved_part == -1 else
+                       entry + ": decode_uniform_kernel + decode_reduce_kernel (uniform split)"
                        if resolved_part == -2 else
-                       "pa_decode: decode_partition_kernel" + (" + decode_reduce_kernel"
+                       entry + ": decode_partition_kernel" + (" + decode_reduce_kernel"
                                                                if resolved_part < max_ctx_bound else
                                                                " (one workgroup per sequence and kv-head)")),
             "bound": "hbm",

@@ -228,6 +228,33 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
                     int32_t max_context_len, float scale, int32_t partition_tokens,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/* One decode step's KV write and attention in one launch ([P2] §3.2.2: step 3
+ * writes the new token's K/V into its slot, step 4 attends over every cached
+ * token, the new one included).  The result — pool contents and out — is that
+ * of pa_write_kv(pool, k_new, v_new, slot_mapping, num_seqs) followed by
+ * pa_decode(...) with the remaining arguments; the attention is bit-identical
+ * to that pair of calls.
+ *   k_new, v_new: device [num_seqs][kv_heads][head_dim] in the pool dtype,
+ *     16-byte aligned: the new token of each sequence, one row per sequence.
+ *   slot_mapping: device int32[num_seqs]; slot_mapping[s] is −1 (nothing to
+ *     write: the token is already in the pool) or the slot of token
+ *     context_lens[s] − 1, the sequence's last, which is what pa_bm_step
+ *     returns.  Live slots are distinct.  A slot outside the pool is skipped.
+ *   The remaining arguments are pa_decode's, with its workspace rules.
+ * The workgroup that attends over the last token of (sequence, kv-head)
+ * writes that row first and reads it back after a barrier, so no second
+ * launch is needed.  The balanced split (PA_PARTITION_BALANCED) has no single
+ * owner of the last token: there the library enqueues pa_write_kv's kernel
+ * before the decode.  A slot that is not the last token's gives undefined
+ * rows (never an access outside the pool); PA_DEBUG_VALIDATE=1 checks the
+ * slots against the tables and lengths on the host.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
+pa_status pa_decode_append(pa_pool* pool, const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                           void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs, int32_t q_heads,
+                           const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                           int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
 /* Sharing-aware decode ([P2] §3.4 and [P1] "跨请求的内存共享": forked samples
  * and beams point their tables at the same physical blocks).  The result is
  * pa_decode's (within fp32 rounding order), for a batch arranged in groups

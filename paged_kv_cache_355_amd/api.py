@@ -144,8 +144,11 @@ def decode_partition_tokens(pool, num_seqs, q_heads, max_context_len, partition_
 
 
 def decode(pool, q, block_tables, context_lens, max_context_len, out=None, out_dtype=None, scale=None,
-           partition_tokens=0, workspace=None, stream=None):
-    """Paged decode attention; returns ``out`` [num_seqs][q_heads][head_dim]."""
+           partition_tokens=0, workspace=None, stream=None, append=None):
+    """Paged decode attention; returns ``out`` [num_seqs][q_heads][head_dim].
+    ``append=(k_new, v_new, slot_mapping)`` runs pa_decode_append: each
+    sequence's new token (its last, row s of k_new/v_new) is written into
+    its slot in the same launch, as pa_write_kv would, before it is attended."""
     import torch
     num_seqs, q_heads, d = (int(x) for x in q.shape)
     if d != pool.head_dim:
@@ -160,12 +163,19 @@ def decode(pool, q, block_tables, context_lens, max_context_len, out=None, out_d
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stride = int(block_tables.shape[1]) if block_tables.dim() == 2 else 0
-    check(lib().pa_decode(pool.handle, _dev_ptr(out, "out", torch_dtype(odt), (num_seqs, q_heads, d)),
-                          DTYPE_CODES[odt], _dev_ptr(q, "q", tdt), num_seqs, q_heads,
-                          _dev_ptr(block_tables, "block_tables", torch.int32), stride,
-                          _dev_ptr(context_lens, "context_lens", torch.int32, (num_seqs,)), int(max_context_len),
-                          float(scale) if scale else 0.0, int(partition_tokens), ws_ptr, ws_len, _stream(stream)),
-          "pa_decode")
+    args = (_dev_ptr(out, "out", torch_dtype(odt), (num_seqs, q_heads, d)), DTYPE_CODES[odt], _dev_ptr(q, "q", tdt),
+            num_seqs, q_heads, _dev_ptr(block_tables, "block_tables", torch.int32), stride,
+            _dev_ptr(context_lens, "context_lens", torch.int32, (num_seqs,)), int(max_context_len),
+            float(scale) if scale else 0.0, int(partition_tokens), ws_ptr, ws_len, _stream(stream))
+    if append is None:
+        check(lib().pa_decode(pool.handle, *args), "pa_decode")
+    else:
+        k_new, v_new, slot_mapping = append
+        shape = (num_seqs, pool.kv_heads, pool.head_dim)
+        check(lib().pa_decode_append(pool.handle, _dev_ptr(k_new, "k_new", tdt, shape),
+                                     _dev_ptr(v_new, "v_new", tdt, shape),
+                                     _dev_ptr(slot_mapping, "slot_mapping", torch.int32, (num_seqs,)), *args),
+              "pa_decode_append")
     return out
 
 

@@ -450,10 +450,14 @@ pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32
   return PA_OK;
 }
 
-pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs,
-                    int32_t q_heads, const int32_t* block_tables, int32_t block_table_stride,
-                    const int32_t* context_lens, int32_t max_context_len, float scale, int32_t partition_tokens,
-                    void* workspace, int64_t workspace_bytes, void* stream) {
+namespace {
+// pa_decode, and pa_decode_append when k_new is not null (then v_new and
+// slot_mapping are its KV write's arguments, checked by the caller).
+pa_status decode_call(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs,
+                      int32_t q_heads, const int32_t* block_tables, int32_t block_table_stride,
+                      const int32_t* context_lens, int32_t max_context_len, float scale, int32_t partition_tokens,
+                      void* workspace, int64_t workspace_bytes, const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, void* stream) {
   if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
   if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "num_seqs must be in [0, 65535]");
   if (num_seqs == 0) return PA_OK;
@@ -482,6 +486,20 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
     if (pa_status s = validate_decode_indices(d, num_seqs, block_tables, block_table_stride, context_lens,
                                               max_context_len, st, &lens, &tables))
       return s;
+    if (k_new) {   // each live slot is the one that holds token len−1 of its sequence
+      std::vector<int32_t> slots;
+      if (pa_status s = fetch_ints(slot_mapping, num_seqs, &slots, st)) return s;
+      for (int32_t i = 0; i < num_seqs; ++i) {
+        const int32_t sl = slots[i], len = lens[i];
+        if (sl < 0) continue;
+        const int32_t want = len > 0 ? tables[static_cast<size_t>(i) * block_table_stride + (len - 1) / d.block_size] *
+                                               d.block_size + (len - 1) % d.block_size
+                                     : -2;
+        if (sl != want)
+          return fail(PA_ERR_INVALID, "slot_mapping[" + std::to_string(i) + "] = " + std::to_string(sl) +
+                                          " is not the slot of token context_lens - 1");
+      }
+    }
     if (plan.balanced) {
       std::vector<int32_t> ctr;
       const int64_t n = int64_t{pa::kMergeLevels} * plan.num_slots;
@@ -512,8 +530,54 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
     a.part_o = reinterpret_cast<float*>(ws + plan.o_off);
     a.unit_desc = plan.uniform ? reinterpret_cast<int32_t*>(ws + plan.desc_off) : nullptr;
   }
+  if (k_new) {
+    if (plan.balanced) {   // its pieces have no single owner of the last token: write first
+      hipError_t e = pa::launch_write_kv(d, k_new, v_new, slot_mapping, num_seqs, st);
+      if (e != hipSuccess) return hip_fail(e, "write_kv launch");
+    } else {
+      a.k_new = k_new;
+      a.v_new = v_new;
+      a.kv_slots = slot_mapping;
+    }
+  }
   hipError_t e = pa::launch_decode(d, a, st);
   return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
+}
+}  // namespace
+
+pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs,
+                    int32_t q_heads, const int32_t* block_tables, int32_t block_table_stride,
+                    const int32_t* context_lens, int32_t max_context_len, float scale, int32_t partition_tokens,
+                    void* workspace, int64_t workspace_bytes, void* stream) {
+  return decode_call(pool, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride, context_lens,
+                     max_context_len, scale, partition_tokens, workspace, workspace_bytes, nullptr, nullptr, nullptr,
+                     stream);
+}
+
+pa_status pa_decode_append(pa_pool* pool, const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                           void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs, int32_t q_heads,
+                           const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                           int32_t max_context_len, float scale, int32_t partition_tokens, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "num_seqs must be in [0, 65535]");
+  if (num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PA_ERR_INVALID, "NULL pointer");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID, "k_new/v_new must be 16-byte aligned");
+  if (debug_validate()) {   // pa_write_kv's own checks of the slots
+    std::vector<int32_t> slots;
+    if (pa_status s = fetch_ints(slot_mapping, num_seqs, &slots, static_cast<hipStream_t>(stream))) return s;
+    const int64_t total = static_cast<int64_t>(pool->d.num_blocks) * pool->d.block_size;
+    std::vector<char> seen(static_cast<size_t>(total), 0);
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t sl = slots[i];
+      if (sl < -1 || sl >= total) return fail(PA_ERR_INVALID, "slot " + std::to_string(sl) + " outside the pool");
+      if (sl >= 0 && seen[sl]++) return fail(PA_ERR_INVALID, "slot " + std::to_string(sl) + " written twice");
+    }
+  }
+  return decode_call(pool, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride, context_lens,
+                     max_context_len, scale, partition_tokens, workspace, workspace_bytes, k_new, v_new, slot_mapping,
+                     stream);
 }
 
 pa_status pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,

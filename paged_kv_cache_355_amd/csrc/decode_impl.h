@@ -388,6 +388,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       const int32_t phys = table[bb + i];
       sh.tbl[i] = static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks) ? phys : -1;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): an append_token store is in L2 before the barrier
     __syncthreads();
     const int32_t tb = max(t_begin, bb * BS);
     const int32_t te = min(t_end, (bb + nb) * BS);
@@ -626,6 +627,7 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
       const int32_t phys = table[bb + i];
       sh.tbl[i] = static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks) ? phys : -1;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): an append_token store is in L2 before the barrier
     __syncthreads();
     const int32_t tb = max(t_begin, bb * BS);
     const int32_t te = min(t_end, (bb + nb) * BS);
@@ -847,6 +849,35 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
 
 // attend_range with the cache policy chosen at run time (wave-uniform): the
 // streaming policy unless the tiles are shared with a neighbouring sequence.
+// The KV write of pa_decode_append ([P2] §3.2.2 step 3, then step 4 in the
+// same launch): the workgroup whose range ends at the context's last token
+// stores that token's K and V rows of kv-head g, k_new/v_new[s][g][:], into
+// slot kv_slots[s] (skipped when the slot is −1 or outside the pool), exactly
+// as write_kv_kernel would.  attend_range waits for every wave's outstanding
+// memory operations (vmcnt(0)) before the barrier that publishes the block
+// ids, which its table loads need anyway; that barrier then orders the stores
+// before every K/V load of the workgroup, so the token is read back from the
+// pool like any other, and the store's round trip overlaps the table loads.
+// The slot must hold token len−1 of sequence s; only this workgroup reads that
+// (block, kv-head) tile, because partitions start on block boundaries.
+template <int DT, int D, int BS>
+__device__ __forceinline__ void append_token(const char* k_pool, const char* v_pool, const char* __restrict__ k_new,
+                                             const char* __restrict__ v_new, const int32_t* __restrict__ kv_slots,
+                                             int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks) {
+  constexpr int ROW = D * Elem<DT>::bytes;   // bytes of one token's row
+  constexpr int L16 = ROW / 16;              // 16-byte pieces per row
+  static_assert(2 * L16 <= 64, "one wave stores both rows");
+  if (threadIdx.x >= 2 * L16) return;
+  const int32_t slot = kv_slots[s];
+  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(num_blocks) * BS) return;
+  const bool is_v = threadIdx.x >= L16;
+  const int piece = threadIdx.x % L16;
+  const int64_t dst = ((static_cast<int64_t>(slot / BS) * kv_heads + g) * BS + slot % BS) * ROW + piece * 16;
+  const int64_t src = (static_cast<int64_t>(s) * kv_heads + g) * ROW + piece * 16;
+  const uint4 v = *reinterpret_cast<const uint4*>((is_v ? v_new : k_new) + src);
+  *reinterpret_cast<uint4*>(const_cast<char*>(is_v ? v_pool : k_pool) + dst) = v;
+}
+
 template <int DT, int D, int BS, int G, int NW, typename Emit>
 __device__ __forceinline__ void attend_range_policy(bool shared, const char* __restrict__ k_pool,
                                                     const char* __restrict__ v_pool, const char* __restrict__ q,
@@ -881,7 +912,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ seq_prefix, int32_t max_prefix, int32_t num_seqs, int32_t num_blocks,
-    int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2) {
+    int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2,
+    const char* __restrict__ k_new, const char* __restrict__ v_new, const int32_t* __restrict__ kv_slots) {
   const int p = blockIdx.x;
   const int g = blockIdx.y;
   const int s = blockIdx.z;
@@ -890,6 +922,10 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
+  // pa_decode_append (no shared prefix there): the last partition owns the
+  // new token; an empty or invalid context's only workgroup still writes it
+  if (kv_slots && p == max(parts_of(len_c, part_tokens), 1) - 1)
+    append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
   if (len_c == 0) {
     if (p == 0) fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
     return;
@@ -1562,12 +1598,15 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t* __restrict__ unit_desc, const int32_t* __restrict__ block_tables, int32_t table_stride,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_blocks, int32_t kv_heads,
-    int32_t max_ctx, float scale_log2) {
+    int32_t max_ctx, float scale_log2, const char* __restrict__ k_new, const char* __restrict__ v_new,
+    const int32_t* __restrict__ kv_slots) {
   const int64_t t = blockIdx.x;
   UniformTask tk;
   if (!uniform_task<BS>(context_lens, num_seqs, kv_heads, max_ctx, t, gridDim.x, &tk)) return;
   const int32_t s = tk.s, g = tk.g;
   const int q_heads = kv_heads * G;
+  if (kv_slots && tk.p == tk.n - 1)   // the unit's last partition owns the new token
+    append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
   if (tk.p == 0 && threadIdx.x == 0) {
     const int64_t u = static_cast<int64_t>(s) * kv_heads + g;
     unit_desc[2 * u] = tk.t0;
@@ -1667,6 +1706,7 @@ void launch_reduce(const DecodeArgs& a, const int32_t* seq_prefix, const int32_t
 
 template <int DT, int D, int BS, int G>
 hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
+  if (a.kv_slots && (a.balanced || a.group_start)) return hipErrorInvalidValue;   // the host writes first there
   if (a.balanced) {
     hipLaunchKernelGGL((decode_balanced_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
                        static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
@@ -1679,7 +1719,8 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
     hipLaunchKernelGGL((decode_uniform_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
                        static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
                        a.out, a.out_dtype, a.part_ml, a.part_o, a.unit_desc, a.block_tables, a.table_stride,
-                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.scale_log2);
+                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.scale_log2,
+                       static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.kv_slots);
     hipError_t e = hipGetLastError();
     // with no more than one workgroup per unit and kv-head nothing splits (uniform_task)
     if (e != hipSuccess || a.grid / p.kv_heads <= a.num_seqs) return e;
@@ -1713,7 +1754,8 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
                      a.table_stride, a.context_lens, seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads,
-                     a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2);
+                     a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2,
+                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.kv_slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || suffix_parts <= 1) return e;
   launch_reduce<D, BS, G>(a, seq_prefix, nullptr, stream);

@@ -63,6 +63,13 @@ struct DecodeArgs {
   int32_t num_groups = 0;
   int32_t max_group_size = 0;
   int32_t max_prefix = 0;
+  // pa_decode_append (whole sequences, fixed partitions or the uniform split):
+  // the workgroup holding sequence s's last token first writes k_new/v_new
+  // [num_seqs][kv_heads][head_dim] row s into slot kv_slots[s].  Null for a
+  // plain decode.
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* kv_slots = nullptr;
 };
 
 // True when the shared-prefix kernels exist for this pool (16-bit K/V, blocks

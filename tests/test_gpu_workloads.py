@@ -70,11 +70,12 @@ def _sample(ids, lens, k, seed):
     return sorted(picks)
 
 
-def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None, shared_prefix=False):
+def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None, shared_prefix=False, append=False):
     """One decode step of workload ``name`` on the GPU, checked against the
     oracle (``partition_tokens`` overrides the workload's split).  With
     ``shared_prefix`` the batch is arranged in the oracle's dispatch order and
-    decoded by pa_decode_shared_prefix with the oracle's prefix groups."""
+    decoded by pa_decode_shared_prefix with the oracle's prefix groups; with
+    ``append`` the KV write and the decode are one pa_decode_append call."""
     import torch
     w = WORKLOADS[name]
     sc = make_scenario(w)
@@ -108,7 +109,9 @@ def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None, shared_
 
     if pairs:
         pk.copy_blocks(pool, torch.tensor(pairs, dtype=torch.int32, device="cuda"))
-    pk.write_kv(pool, k_new, v_new, torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda())
+    slots_dev = torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda()
+    if not append:
+        pk.write_kv(pool, k_new, v_new, slots_dev)
     part = w.partition_tokens if partition_tokens is None else partition_tokens
     if shared_prefix:
         starts, prefix, largest = ora.prefix_groups(ids)
@@ -119,7 +122,7 @@ def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None, shared_
                                       partition_tokens=part)
     else:
         out = pk.decode(pool, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), max_len,
-                        partition_tokens=part)
+                        partition_tokens=part, append=(k_new, v_new, slots_dev) if append else None)
     torch.cuda.synchronize()
 
     # pool bytes after the step: oracle copy + write on the host copy of the start state
@@ -220,3 +223,21 @@ def test_long_splitk_bf16_full(gpu, partition):
     """The long-context batch with the workload's 512-token partitions and
     with the uniform split (~1100-token partitions, one resident grid)."""
     run_step(gpu, "long_splitk_bf16", samples=3, partition_tokens=partition)
+
+
+@pytest.mark.parametrize("name,partition,cow_step", [
+    ("mha7b_fp16", None, False),
+    ("gqa70b_bf16", None, False),
+    ("gqa70b_bf16", 512, False),
+    ("gqa70b_bf16", -2, False),
+    ("gqa70b_bf16", -1, False),
+    ("prefix_share_fp16", None, True),
+    ("long_splitk_bf16", None, False),
+    ("long_splitk_bf16", -2, False),
+])
+def test_decode_append_full(gpu, name, partition, cow_step):
+    """The step as pa_decode_append (KV write inside the decode launch): whole
+    sequences, fixed partitions, the uniform split, and the balanced split
+    (where the library writes first); the pool is checked bit for bit and the
+    outputs against the oracle, as for the two-call step."""
+    run_step(gpu, name, cow_step=cow_step, samples=4, partition_tokens=partition, append=True)
