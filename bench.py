@@ -19,8 +19,8 @@ the workload's shape, resident in HBM before timing starts.
 Printed: one JSON line.  ``value`` is KV bytes read by decode per second of
 the whole timed region (host step, copies and kernels included);
 ``roofline`` is the decode call alone, timed with HIP events on its stream
-around the first layer's call of every timed step (``--timed-layers all``
-brackets every layer's; each event pair costs the step about 5 us);
+around one layer's call per timed step, the layer rotating (``--timed-layers
+all`` brackets every layer's; each event pair costs the step about 5 us);
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
@@ -63,8 +63,8 @@ def parse_args():
                          "that many tokens")
     ap.add_argument("--decode", choices=["auto", "plain", "shared"], default="auto",
                     help="auto = pa_decode_shared_prefix when the batch has prefix groups, else pa_decode")
-    ap.add_argument("--timed-layers", choices=["first", "all"], default="first",
-                    help="decode calls bracketed by HIP events: the first layer's of every step (default) "
+    ap.add_argument("--timed-layers", choices=["one", "all"], default="one",
+                    help="decode calls bracketed by HIP events: one layer's per step, rotating (default), "
                          "or every layer's")
     ap.add_argument("--fused-append", action="store_true",
                     help="one pa_decode_append call per layer (KV write inside the decode launch) instead of "
@@ -193,7 +193,7 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
             if not fused:
                 check(L.pa_write_kv(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
                                     dev["slots"].data_ptr(), B, sptr), "pa_write_kv")
-            timed = timing is not None and (timing["all_layers"] or layer == 0)
+            timed = timing is not None and (timing["all_layers"] or layer == (step0 + i) % len(st["pools"]))
             if timed:
                 ev0, ev1 = timing["free"].pop()
                 ev0.record(stream)
@@ -501,8 +501,9 @@ def main():
     run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None, shared_prefix, args.fused_append)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    # HIP events around the decode call of the first layer of every step (or of
-    # every layer): each recorded pair adds about 5 us of GPU time to a step
+    # HIP events around one layer's decode call per step, the layer rotating
+    # from step to step (or around every layer's): each recorded pair adds
+    # about 5 us of GPU time to a step
     timing = {"used": [], "all_layers": args.timed_layers == "all",
               "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(args.steps * args.layers)]}
