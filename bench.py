@@ -72,6 +72,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-admission (bulk pa_write_kv) probe")
     ap.add_argument("--no-swap", action="store_true", help="skip the block swap (pa_swap_out / pa_swap_in) probe")
+    ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write (pa_copy_blocks) probe")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run a plain elementwise copy of this many MiB three times "
@@ -406,6 +407,58 @@ def prefill_probe(pk, w, st, reps=5):
             "bytes": "K and V of every prompt token, read from the staging tensors and written into the pool"}
 
 
+def cow_probe(pk, w, st, reps=5):
+    """Copy-on-write at a fork: the prefix-sharing workload's first step after
+    the fork copies every shared, part-filled last block (pa_bm_step's pairs,
+    224 for 32 prompts x 8 samples).  A workload without forks copies each
+    sequence's last block into a free block, as a fork of the whole batch
+    would.  pa_copy_blocks on the first layer's pool; repeating the same
+    pairs is idempotent."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_355_amd._lib import lib, check
+    from workloads import make_scenario
+
+    pool = st["pools"][0]
+    sc = make_scenario(w)
+    if sc.cow_step is not None:
+        bm = pk.BlockManager(sc.num_blocks, w.block_size, sc.free_order)
+        for op in sc.setup:
+            if op[0] == "add":
+                bm.add_seq(op[1], op[2])
+            else:
+                bm.fork(op[1], op[2])
+        pairs = bm.step(sc.cow_step)[1]
+        source = "the fork step's copy-on-write pairs (pa_bm_step)"
+    else:
+        free = st["bm"].free_list()
+        last = [st["bm"].block_table(s)[0][-1] for s in st["ids"][:len(free)]]
+        pairs = np.stack([np.asarray(last, dtype=np.int32), np.asarray(free[:len(last)], dtype=np.int32)], axis=1)
+        source = "each sequence's last block into a free block"
+    n = int(pairs.shape[0])
+    if n == 0:
+        return None
+    pairs_dev = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+    L = lib()
+    check(L.pa_copy_blocks(pool.handle, pairs_dev.data_ptr(), n, stream.cuda_stream), "pa_copy_blocks")   # warm-up
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        check(L.pa_copy_blocks(pool.handle, pairs_dev.data_ptr(), n, stream.cuda_stream), "pa_copy_blocks")
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    moved = 2 * 2 * n * pool.block_bytes   # K and V blocks, read + written
+    sources = int(np.unique(pairs[:, 0]).shape[0])
+    unique = 2 * (sources + n) * pool.block_bytes   # each source read once, each destination written
+    return {"pairs": n, "distinct_sources": sources, "pairs_from": source, "copy_blocks_us": round(us, 2),
+            "copy_blocks_GBps": round(moved / us / 1e3, 1), "unique_GBps": round(unique / us / 1e3, 1),
+            "unique_frac_of_hbm_peak": round(unique / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "bytes": "copy_blocks_GBps: K and V of every pair's source read and destination written; "
+                     "unique_GBps: each distinct source read once (a shared block's later copies hit cache)"}
+
+
 def swap_probe(pk, st, target_mib=256, reps=3):
     """Block swap between the first layer's pool and pinned host memory: about
     target_mib MiB of whole blocks out (pa_swap_out) and back into the same
@@ -585,6 +638,8 @@ def main():
         result["prefill"] = prefill_probe(pk, w, st)
     if not args.no_swap:
         result["swap"] = swap_probe(pk, st)
+    if not args.no_cow:
+        result["copy_on_write"] = cow_probe(pk, w, st)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
