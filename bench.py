@@ -73,7 +73,8 @@ def parse_args():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-admission (bulk pa_write_kv) probe")
     ap.add_argument("--no-swap", action="store_true", help="skip the block swap (pa_swap_out / pa_swap_in) probe")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write (pa_copy_blocks) probe")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="the CPU oracle sample repeats whole steps until this many seconds have passed")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run a plain elementwise copy of this many MiB three times "
                          "(calibrates HBM byte counters)")
@@ -288,7 +289,7 @@ def cpu_baseline(w, sc, budget_s):
     times, kv = [], []
     with threadpool_limits(limits=1):
         t_start = time.perf_counter()
-        while not times or (time.perf_counter() - t_start < budget_s and len(times) < 3):
+        while not times or time.perf_counter() - t_start < budget_s:
             t0 = time.perf_counter()
             slots, pairs = ora.step(ids)
             oracle_copy_blocks(k_pool, v_pool, pairs)
