@@ -213,6 +213,32 @@ def test_decode_shared_prefix_matches_private_copy(gpu):
     assert np.max(np.abs(got[0] - got[1])) <= 1e-6 and np.max(np.abs(got[0] - got[2])) <= 1e-6
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("group", [1, 8])
+def test_split_modes_agree_to_fp32_rounding(gpu, dtype, group):
+    """Splitting a context changes only the order of the fp32 merges ([P2]
+    §4.1: partial maxima and sums combine exactly), so whole sequences, fixed
+    partitions of one block and of 512 tokens, the uniform and the balanced
+    split agree with each other to fp32 rounding, far inside the oracle's
+    2e-3: within 2^-20 of the largest output.  Measured on MI355X: about 2^-26
+    on the vector loop and 2^-23 on the matrix-core loop (16-bit K/V, 8 rows),
+    whose softmax weights are split into a 16-bit head and a 16-bit remainder
+    relative to each partition's maximum."""
+    pk = gpu
+    lens = [2999, 1, 16, 17, 513, 1024, 0, 777, 2048, 5]
+    case = build_case(lens, 2, group, 128, 16, dtype, 4242 + group, scale=128 ** -0.5)
+    outs = {}
+    for part in (3008, 16, 512, pk.PA_PARTITION_UNIFORM, pk.PA_PARTITION_BALANCED):
+        outs[part] = out_to_f64(run_decode(pk, case, 2, 128, 16, dtype, out_dtype="f32", partition_tokens=part))
+    ref = outs[3008]   # one partition holds the longest context: nothing is split
+    scale = float(np.max(np.abs(ref)))
+    bound = scale * 2.0 ** -20
+    for part, got in outs.items():
+        diff = float(np.max(np.abs(got - ref)))
+        print(f"[split modes] {dtype} G{group} partition {part}: max |diff| {diff:.3e} (bound {bound:.3e})", flush=True)
+        assert diff <= bound, (part, diff)
+
+
 @pytest.mark.parametrize("grid", [1, 3, 37, 4000])
 def test_balanced_split_any_grid(gpu, grid):
     """The balanced split is exact for any number of workgroups: one workgroup
