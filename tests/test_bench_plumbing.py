@@ -1,0 +1,60 @@
+"""The measurement plumbing of bench.py that runs without a GPU: the one-GPU
+contract, the kernel-source hash that ties recorded HBM counters to the code
+they were taken on, and the recorded counter summaries themselves."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+WORKLOADS = ["mha7b_fp16", "gqa70b_bf16", "prefix_share_fp16", "long_splitk_bf16"]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                          text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr and proc.stdout == ""
+
+
+def test_kernel_hash_ignores_comments_and_blank_space(tmp_path, monkeypatch):
+    src = open(bench.KERNEL_SOURCE, encoding="utf-8").read()
+    base = bench.kernel_source_hash()
+    edited = tmp_path / "commented.h"
+    edited.write_text("// a new comment line\n\n" + src.replace("\n", "   // trailing note\n", 3), encoding="utf-8")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(edited))
+    assert bench.kernel_source_hash() == base
+    changed = tmp_path / "changed.h"
+    changed.write_text(src + "\nconstexpr int kUnused = 1;\n", encoding="utf-8")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(changed))
+    assert bench.kernel_source_hash() != base
+
+
+@pytest.mark.parametrize("workload", WORKLOADS)
+def test_recorded_traffic_summaries_are_consistent(workload):
+    """Each summary ends with the record bench.py reads: HBM bytes from the
+    two counters scaled by the copy-kernel calibration, close to (and not
+    below) the algorithmic bytes of the counted run."""
+    path = os.path.join(bench.PROFILES, f"decode_{workload}_traffic.txt")
+    text = open(path, encoding="utf-8").read()
+    assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text
+    rec = json.loads([line for line in text.splitlines() if line.startswith("{")][-1])
+    for key in ("kernel_source_sha256", "decode", "hbm_bytes_per_call", "algorithmic_bytes_per_call",
+                "fetch_factor", "write_factor"):
+        assert key in rec, key
+    assert rec["decode"] in ("pa_decode", "pa_decode_shared_prefix", "pa_decode_append")
+    assert abs(rec["fetch_factor"] - 2.0) < 0.05 and abs(rec["write_factor"] - 1.0) < 0.05
+    ratio = rec["hbm_bytes_per_call"] / rec["algorithmic_bytes_per_call"]
+    assert 1.0 <= ratio <= 1.1, ratio
+    # bench.py uses the record only for the code it was taken on
+    got = bench.recorded_traffic(workload, rec["decode"])
+    if rec["kernel_source_sha256"] == bench.kernel_source_hash():
+        assert got == (rec["hbm_bytes_per_call"], round(ratio, 4))
+    else:
+        assert got == (None, None)
