@@ -1749,7 +1749,13 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   const int32_t suffix_parts =
       static_cast<int32_t>(std::max<int64_t>(1, (static_cast<int64_t>(a.max_context_len) + a.partition_tokens - 1) /
                                                     a.partition_tokens));
-  dim3 grid(suffix_parts, p.kv_heads, a.num_seqs);
+  // Workgroup w runs on XCD w mod 8 and the partition index varies fastest, so
+  // with an even count the first partitions of all (sequence, kv-head) units
+  // (often the only ones a short context has) would gather on half, a quarter
+  // or an eighth of the XCDs.  An odd count spreads them over all eight; the
+  // extra column's workgroups return at once, like any partition past a
+  // context's end.
+  dim3 grid(suffix_parts | 1, p.kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
                      static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
