@@ -70,7 +70,7 @@ def _sample(ids, lens, k, seed):
     return sorted(picks)
 
 
-def run_step(pk, name, cow_step=False, samples=6, partition_tokens=None, shared_prefix=False, append=False):
+def run_step(pk, name, cow_step=False, samples=16, partition_tokens=None, shared_prefix=False, append=False):
     """One decode step of workload ``name`` on the GPU, checked against the
     oracle (``partition_tokens`` overrides the workload's split).  With
     ``shared_prefix`` the batch is arranged in the oracle's dispatch order and
@@ -200,7 +200,7 @@ def test_gqa70b_bf16_split_full(gpu, partition):
 
 
 def test_prefix_share_cow_step_full(gpu):
-    r = run_step(gpu, "prefix_share_fp16", cow_step=True, samples=10)
+    r = run_step(gpu, "prefix_share_fp16", cow_step=True, samples=16)
     assert len(r["pairs"]) == 224
 
 
@@ -214,7 +214,7 @@ def test_prefix_share_shared_prefix_decode_full(gpu, cow_step):
     """The prefix-sharing batch (32 prompts x 8 samples) through the
     sharing-aware decode: each prompt's 1024-token prefix read once per
     kv-head, checked on sampled sequences against the oracle."""
-    r = run_step(gpu, "prefix_share_fp16", cow_step=cow_step, samples=10, shared_prefix=True)
+    r = run_step(gpu, "prefix_share_fp16", cow_step=cow_step, samples=16, shared_prefix=True)
     assert len(r["pairs"]) == (224 if cow_step else 0)
 
 
@@ -222,7 +222,7 @@ def test_prefix_share_shared_prefix_decode_full(gpu, cow_step):
 def test_long_splitk_bf16_full(gpu, partition):
     """The long-context batch with the workload's 512-token partitions and
     with the uniform split (~1100-token partitions, one resident grid)."""
-    run_step(gpu, "long_splitk_bf16", samples=3, partition_tokens=partition)
+    run_step(gpu, "long_splitk_bf16", samples=8, partition_tokens=partition)
 
 
 @pytest.mark.parametrize("name,partition,cow_step", [
