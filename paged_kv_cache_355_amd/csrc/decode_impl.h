@@ -1129,22 +1129,50 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(void* __r
   __shared__ float sh_red[kReduceThreads / 64];
   __shared__ float sh_w[kReduceLds];
   __shared__ float sh_acc[LANES][DC];
-  float mm = kNegBig;
-  for (int p = tid; p < nparts; p += kReduceThreads) mm = fmaxf(mm, ml[p * mls]);
-  const float M = block_reduce_max(mm, sh_red);
-  float part = 0.f;
-  for (int p = tid; p < nparts; p += kReduceThreads) {
-    const float wgt = exp2f_fast(ml[p * mls] - M);
-    if (p < kReduceLds) sh_w[p] = wgt;
-    part += ml[p * mls + 1] * wgt;   // a NaN sum marks a partition that met a bad block id
-  }
-  const float L = block_reduce_sum(part, sh_red);   // its barriers also publish sh_w
   const int dl = tid % DC;
   const int d = d0 + dl;
   const int pl = tid / DC;
-  // four independent accumulators keep four loads in flight per thread
+  // This thread's first kPre output values do not depend on the weights:
+  // their loads leave before the reductions below and overlap them.
+  constexpr int kPre = 8;
+  float pre_o[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int pp = pl + k * LANES;
+    pre_o[k] = pp < nparts ? po[pp * pos + d] : 0.f;
+  }
+  // (max, sum) of partition tid, kept for the weight pass
+  const bool own = tid < nparts;
+  const float m0 = own ? ml[tid * mls] : kNegBig;
+  const float l0 = own ? ml[tid * mls + 1] : 0.f;
+  float mm = m0;
+  for (int p = tid + kReduceThreads; p < nparts; p += kReduceThreads) mm = fmaxf(mm, ml[p * mls]);
+  const float M = block_reduce_max(mm, sh_red);
+  float part = 0.f;
+  if (own) {
+    const float wgt = exp2f_fast(m0 - M);
+    if (tid < kReduceLds) sh_w[tid] = wgt;
+    part += l0 * wgt;   // a NaN sum marks a partition that met a bad block id
+  }
+  for (int p = tid + kReduceThreads; p < nparts; p += kReduceThreads) {
+    const float wgt = exp2f_fast(ml[p * mls] - M);
+    if (p < kReduceLds) sh_w[p] = wgt;
+    part += ml[p * mls + 1] * wgt;
+  }
+  const float L = block_reduce_sum(part, sh_red);   // its barriers also publish sh_w
+  // four independent accumulators keep four loads in flight per thread; the
+  // k-th partition of this lane goes to accumulator k mod 4 throughout
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int p = pl;
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int pp = pl + k * LANES;
+    if (pp < nparts) {
+      const float wgt = pp < kReduceLds ? sh_w[pp] : exp2f_fast(ml[pp * mls] - M);
+      acc[k & 3] = __builtin_fmaf(wgt, pre_o[k], acc[k & 3]);
+    }
+  }
+  static_assert(kPre % 4 == 0, "the loop below continues the accumulator rotation");
+  int p = pl + kPre * LANES;
   for (; p + 3 * LANES < nparts; p += 4 * LANES) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
