@@ -104,3 +104,44 @@ def test_random_case_matches_oracle(gpu, i):
     for s, n in enumerate(c["lens"]):
         if n == 0:
             assert np.all(got[s] == 0.0)
+
+
+N_FAMILY_CASES = 24
+
+
+def draw_families(i):
+    rng = np.random.default_rng(80000 + i)
+    dtype = ["f32", "f16", "bf16"][rng.integers(3)] if rng.random() < 0.2 else ["f16", "bf16"][rng.integers(2)]
+    bs = [4, 16, 32, 64][rng.integers(4)] if rng.random() < 0.25 else [16, 32][rng.integers(2)]
+    group = [1, 2, 4, 8][rng.integers(4)]
+    kv_heads = [1, 2, 3][rng.integers(3)]
+    head_dim = [64, 128][rng.integers(2)]
+    fams = []
+    for _ in range(int(rng.integers(1, 6))):
+        prompt = int(rng.integers(1, 700)) if rng.random() < 0.8 else int(rng.integers(1, 8)) * bs
+        members = int(rng.integers(1, 21))
+        fams.append((prompt, [int(x) for x in rng.integers(0, 120, size=members)]))
+    part = 0 if rng.random() < 0.5 else int(rng.integers(1, 20)) * bs
+    return dict(dtype=dtype, bs=bs, group=group, kv_heads=kv_heads, head_dim=head_dim, families=fams,
+                partition=part, seed=81000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_FAMILY_CASES))
+def test_random_forked_batch_through_shared_prefix_decode(gpu, i):
+    """Random fork families (prompts of any length, 1-20 members, 0-119
+    appended tokens each, so copy-on-write at part-filled shared blocks) in the
+    oracle's dispatch order and prefix groups, through pa_decode_shared_prefix
+    (fp32 pools and blocks under 16 tokens take the plain decode inside)."""
+    from tests.gpu_util import build_families, run_shared_prefix
+    pk = gpu
+    c = draw_families(i)
+    print(f"[family fuzz {i}] {c}", flush=True)
+    case = build_families(c["families"], c["kv_heads"], c["group"], c["head_dim"], c["bs"], c["dtype"], c["seed"],
+                          scale=c["head_dim"] ** -0.5)
+    got = out_to_f64(run_shared_prefix(pk, case, c["kv_heads"], c["head_dim"], c["bs"], c["dtype"], out_dtype="f32",
+                                       partition_tokens=c["partition"]))
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], c["dtype"])
+    err = float(np.max(np.abs(got - want)))
+    print(f"[family fuzz {i}] groups {len(case['group_start']) - 1}, max prefix {int(case['prefix'].max())}, "
+          f"max |err| {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and err <= TOL[c["dtype"]]
