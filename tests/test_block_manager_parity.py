@@ -227,3 +227,57 @@ class ParityMachine(RuleBasedStateMachine):
 
 TestParityMachine = ParityMachine.TestCase
 TestParityMachine.settings = settings(max_examples=120, stateful_step_count=40, deadline=None)
+
+
+def test_beam_search_fork_free_churn():
+    """Beam search: each request's prompt forks into W beams; every step all
+    live beams append one token together (copy-on-write where a beam's last
+    block is still shared), then each request keeps a seeded random subset of
+    its beams, frees the rest and refills its width by forking survivors.
+    Blocks churn between the free list and up to W sharers; the library and
+    the oracle must agree on every slot, copy pair, table, refcount and the
+    free list after every step."""
+    rng = np.random.default_rng(2024)
+    requests, width, steps, bs = 6, 4, 60, 8
+    nb = requests * width * (-(-(40 + steps) // bs) + 2)
+    order = rng.permutation(nb)
+    lib_bm = pk.BlockManager(nb, bs, order)
+    ora = OracleBlockManager(nb, bs, order)
+    next_id = 0
+    beams = {}
+    for r in range(requests):
+        root = next_id
+        next_id += 1
+        n = int(rng.integers(1, 40))
+        lib_bm.add_seq(root, n)
+        ora.add_seq(root, n)
+        beams[r] = [root]
+        for _ in range(width - 1):
+            lib_bm.fork(root, next_id)
+            ora.fork(root, next_id)
+            beams[r].append(next_id)
+            next_id += 1
+    assert_same_state(lib_bm, ora)
+    copies = 0
+    for _ in range(steps):
+        ids = sorted(b for r in beams for b in beams[r])
+        s1, p1, _, _ = lib_bm.step(ids)
+        s2, p2 = ora.step(ids)
+        assert s1.tolist() == s2
+        assert [tuple(x) for x in p1.tolist()] == p2
+        copies += len(p2)
+        for r in beams:
+            keep = sorted(rng.choice(beams[r], size=int(rng.integers(1, width + 1)), replace=False).tolist())
+            for b in beams[r]:
+                if b not in keep:
+                    lib_bm.free_seq(b)
+                    ora.free_seq(b)
+            while len(keep) < width:
+                parent = int(rng.choice(keep))
+                lib_bm.fork(parent, next_id)
+                ora.fork(parent, next_id)
+                keep.append(next_id)
+                next_id += 1
+            beams[r] = keep
+        assert_same_state(lib_bm, ora)
+    assert copies > 0 and lib_bm.stats()["shared_blocks"] > 0
