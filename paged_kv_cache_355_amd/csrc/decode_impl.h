@@ -1760,8 +1760,10 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
     if constexpr (DT != kF32 && BS >= 16) {
       const int32_t tiles = (a.max_group_size + 16 / G - 1) / (16 / G);
       const int32_t prefix_parts = (a.max_prefix + a.partition_tokens - 1) / a.partition_tokens;
+      // an odd count of prefix partitions, for the reason given at the
+      // partition kernel's launch below (parts past a prefix return at once)
       hipLaunchKernelGGL((decode_prefix_kernel<DT, D, BS, G, kWaves>),
-                         dim3(prefix_parts, p.kv_heads * tiles, a.num_groups), dim3(kThreads), 0, stream,
+                         dim3(prefix_parts | 1, p.kv_heads * tiles, a.num_groups), dim3(kThreads), 0, stream,
                          static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
                          a.part_ml, a.part_o, a.block_tables, a.table_stride, a.context_lens, a.group_start,
                          a.seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len,
