@@ -1341,6 +1341,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
     int32_t max_ctx, int32_t num_slots, float scale_log2) {
   constexpr int NT = NW * 64;
   constexpr int CT = Chunk<DT, D, BS>::CT;
+  // slices are cut at multiples of CT; the matrix-core loop reads 16-token tiles
+  static_assert(!kUseMfma<DT, BS, G> || CT % 16 == 0, "balanced slices must hold whole matrix-core tiles");
   const int64_t w = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t q_heads = kv_heads * G;
