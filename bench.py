@@ -73,6 +73,7 @@ def parse_args():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-admission (bulk pa_write_kv) probe")
     ap.add_argument("--no-swap", action="store_true", help="skip the block swap (pa_swap_out / pa_swap_in) probe")
     ap.add_argument("--no-cow", action="store_true", help="skip the copy-on-write (pa_copy_blocks) probe")
+    ap.add_argument("--no-read-probe", action="store_true", help="skip the streaming-read reference")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="the CPU oracle sample repeats whole steps until this many seconds have passed")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -460,6 +461,25 @@ def cow_probe(pk, w, st, reps=5):
                      "unique_GBps: each distinct source read once (a shared block's later copies hit cache)"}
 
 
+def stream_read_probe(gib=2, reps=10):
+    """A plain streaming read measured on this GPU: torch's sum over a 2 GiB
+    buffer viewed as int64 (default cache policy), the median of reps calls."""
+    import torch
+    n = gib << 30
+    x = torch.ones(n // 8, dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        x.sum()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        x.sum()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+    del x
+    return round(n / (ms * 1e-3) / 1e9, 1)
+
+
 def swap_probe(pk, st, target_mib=256, reps=3):
     """Block swap between the first layer's pool and pinned host memory: about
     target_mib MiB of whole blocks out (pa_swap_out) and back into the same
@@ -641,6 +661,11 @@ def main():
         result["swap"] = swap_probe(pk, st)
     if not args.no_cow:
         result["copy_on_write"] = cow_probe(pk, w, st)
+    if not args.no_read_probe:
+        read_gbps = stream_read_probe()
+        result["stream_read_probe"] = {"GBps": read_gbps, "decode_over_probe": round(achieved / read_gbps, 4),
+                                       "kernel": "torch.sum over a 2 GiB buffer viewed as int64 (default cache "
+                                                 "policy), median of 10; a measured streaming-read rate of this GPU"}
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
