@@ -397,6 +397,31 @@ def test_decode_bad_table_entry_gives_nan_not_a_fault(gpu, partition):
     assert np.max(np.abs(got[[0, 2]] - want[[0, 2]])) <= TOL["f16"]
 
 
+def test_partition_length_from_the_environment(gpu):
+    """PA_PARTITION_TOKENS sets the length the automatic choice (partition_tokens
+    0) uses, so a deployment can pin it without code changes; an explicit
+    length or split mode from the caller wins, and a length that is not a
+    multiple of the block size is an error."""
+    pk = gpu
+    lens = [700, 1, 0, 129, 1500]
+    case = build_case(lens, 2, 4, 128, 16, "bf16", 606, scale=128 ** -0.5)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "bf16")
+    pool = pk.Pool(case["num_blocks"], 16, 2, 128, "bf16")
+    os.environ["PA_PARTITION_TOKENS"] = "64"
+    try:
+        assert pk.decode_partition_tokens(pool, len(lens), 8, 1500, 0) == 64
+        assert pk.decode_partition_tokens(pool, len(lens), 8, 1500, 256) == 256
+        assert pk.decode_partition_tokens(pool, len(lens), 8, 1500, pk.PA_PARTITION_UNIFORM) == pk.PA_PARTITION_UNIFORM
+        got = out_to_f64(run_decode(pk, case, 2, 128, 16, "bf16", out_dtype="f32", partition_tokens=0))
+        assert np.max(np.abs(got - want)) <= TOL["bf16"]
+        os.environ["PA_PARTITION_TOKENS"] = "24"
+        with pytest.raises(pk.PaError):
+            pk.decode_partition_tokens(pool, len(lens), 8, 1500, 0)
+    finally:
+        del os.environ["PA_PARTITION_TOKENS"]
+    assert pk.decode_partition_tokens(pool, len(lens), 8, 1500, 0) == pk.PA_PARTITION_UNIFORM
+
+
 def test_decode_empty_batch_and_argument_errors(gpu):
     import torch
     pk = gpu
