@@ -212,13 +212,15 @@ pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void
  *     with pa_bm_dispatch_order to run long sequences first.  Results do not
  *     depend on the order.
  *   workspace: device memory of ≥ pa_decode_workspace_bytes(...) bytes,
- *     256-byte aligned; may be NULL when that is 0.  The balanced split keeps
- *     merge counters at the end of the workspace_bytes it is given: a new
- *     workspace must be zero-filled once before its first use, and every call
- *     leaves the counters at zero again, so the workspace can be reused by
- *     later calls on the same pool with the same q_heads and any sizes up to
- *     those it was sized for.  Calls that may run concurrently need separate
- *     workspaces.
+ *     256-byte aligned; may be NULL when that is 0.  Its first 48 KiB
+ *     (whenever the size is not 0) hold the balanced split's merge counters;
+ *     partial results of every split mode follow them.  A new workspace must
+ *     be zero-filled once before its first use (at least those 48 KiB); every
+ *     call leaves the counters at zero again and no split mode writes them
+ *     otherwise, so one workspace serves later calls on the same pool of any
+ *     split mode and any sizes whose pa_decode_workspace_bytes (or
+ *     pa_decode_shared_prefix_workspace_bytes) fits in it.  Calls that may
+ *     run concurrently need separate workspaces.
  * A length above max_context_len, or a block id outside the pool, yields NaN
  * in that sequence's output rows instead of a memory access out of bounds.
  * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
@@ -277,9 +279,10 @@ pa_status pa_decode_append(pa_pool* pool, const void* k_new, const void* v_new, 
  *     prefixes and the rest; 0 = whole contexts when the batch fills the
  *     device, else 512.  PA_PARTITION_BALANCED is rejected.
  *   workspace: ≥ pa_decode_shared_prefix_workspace_bytes(...) bytes, 256-byte
- *     aligned, zero-filled once before first use as for pa_decode (the
- *     shared-prefix kernels only write partial results there; the fallback
- *     below may take pa_decode's balanced split, whose counters live there).
+ *     aligned, zero-filled once before first use, laid out and shareable as
+ *     for pa_decode (the shared-prefix kernels write partial results after
+ *     the counter region; the fallback below may take pa_decode's balanced
+ *     split, which counts there).
  * Pools with fp32 K/V or blocks under 16 tokens, and max_prefix_tokens = 0,
  * take pa_decode itself (the grouping arguments are then ignored).  A
  * violated grouping contract gives wrong rows, never an out-of-bounds

@@ -79,7 +79,10 @@ pa_status fetch_ints(const int32_t* dev, int64_t n, std::vector<int32_t>* host, 
 }
 
 // How pa_decode splits the work for these sizes, and where its workspace
-// pieces sit.
+// pieces sit.  Every plan that keeps partial results reserves the balanced
+// split's merge counters at the front of the workspace (kCounterBytes, used
+// only by that split) and lays its records out after them, so no split mode
+// writes where another one counts.
 struct DecodePlan {
   bool balanced = false;
   bool uniform = false;          // uniform split: `grid` workgroups, unit descriptors at desc_off
@@ -88,10 +91,17 @@ struct DecodePlan {
   int32_t max_parts = 1;
   int32_t grid = 0;              // balanced split
   int32_t num_slots = 0;
-  int64_t ml_off = 0, o_off = 0, counters_bytes = 0, bytes = 0;
+  int64_t ml_off = 0, o_off = 0, bytes = 0;
 };
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Record layout after the counter region: (max, sum) rows, then output rows.
+void layout_records(DecodePlan* plan, int64_t rows, int32_t head_dim) {
+  plan->ml_off = pa::kCounterBytes;
+  plan->o_off = plan->ml_off + round256(rows * 2 * 4);
+  plan->bytes = plan->o_off + rows * head_dim * 4;
+}
 
 // How to split: an explicit positive partition length (a multiple of
 // block_size), PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM; for 0, the
@@ -128,12 +138,7 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
                                       std::to_string(d.block_size) + ")");
     plan->partition_tokens = p;
     plan->max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, p)));
-    if (plan->max_parts > 1) {
-      const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts;
-      plan->ml_off = 0;
-      plan->o_off = round256(rows * 2 * 4);
-      plan->bytes = plan->o_off + rows * d.head_dim * 4;
-    }
+    if (plan->max_parts > 1) layout_records(plan, static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts, d.head_dim);
     return PA_OK;
   }
   if (uniform) {
@@ -147,10 +152,8 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
     if (W >= (int64_t{1} << 31)) return fail(PA_ERR_INVALID, "too many sequences x kv-heads");
     plan->uniform = true;
     plan->grid = static_cast<int32_t>(W);
-    const int64_t rows = W * group;
-    plan->ml_off = 0;
-    plan->o_off = round256(rows * 2 * 4);
-    plan->desc_off = round256(plan->o_off + rows * d.head_dim * 4);
+    layout_records(plan, W * group, d.head_dim);
+    plan->desc_off = round256(plan->bytes);
     plan->bytes = plan->desc_off + units * 2 * 4;
     return PA_OK;
   }
@@ -161,15 +164,7 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
   if (units + grid >= (int64_t{1} << 31)) return fail(PA_ERR_INVALID, "too many sequences x kv-heads");
   plan->grid = grid;
   plan->num_slots = static_cast<int32_t>(units + grid);
-  const int64_t slots = plan->num_slots;
-  // Records from the front, merge counters against the end of the workspace
-  // the caller passes: a smaller call's counters then lie inside a larger
-  // call's counter area, never on its records, so one zero-filled workspace
-  // serves every call of one pool and q_heads up to the sizes it was made for.
-  plan->ml_off = 0;
-  plan->o_off = round256(slots * group * 2 * 4);
-  plan->counters_bytes = int64_t{pa::kMergeLevels} * slots * 4;
-  plan->bytes = plan->o_off + slots * group * d.head_dim * 4 + plan->counters_bytes;
+  layout_records(plan, static_cast<int64_t>(plan->num_slots) * group, d.head_dim);
   return PA_OK;
 }
 
@@ -201,10 +196,7 @@ pa_status plan_shared_prefix(const pa_pool* pool, int32_t num_seqs, int32_t q_he
                                     std::to_string(d.block_size) + ")");
   plan->partition_tokens = p;
   plan->max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_prefix, p) + ceil_div(max_context_len, p)));
-  const int64_t rows = static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts;
-  plan->ml_off = 0;
-  plan->o_off = round256(rows * 2 * 4);
-  plan->bytes = plan->o_off + rows * d.head_dim * 4;
+  layout_records(plan, static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts, d.head_dim);
   return PA_OK;
 }
 
@@ -502,12 +494,8 @@ pa_status decode_call(const pa_pool* pool, void* out, pa_dtype out_dtype, const 
     }
     if (plan.balanced) {
       std::vector<int32_t> ctr;
-      const int64_t n = int64_t{pa::kMergeLevels} * plan.num_slots;
-      const int64_t counters_off = (workspace_bytes & ~int64_t{3}) - plan.counters_bytes;
-      if (pa_status s = fetch_ints(reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
-                                                                    counters_off),
-                                   n, &ctr, st))
-        return s;
+      const int64_t n = pa::kCounterBytes / 4;
+      if (pa_status s = fetch_ints(static_cast<const int32_t*>(workspace), n, &ctr, st)) return s;
       for (int64_t i = 0; i < n; ++i)
         if (ctr[static_cast<size_t>(i)] != 0)
           return fail(PA_ERR_INVALID, "workspace merge counters are not zero (zero-fill a new workspace once)");
@@ -523,9 +511,7 @@ pa_status decode_call(const pa_pool* pool, void* out, pa_dtype out_dtype, const 
   a.max_parts = plan.max_parts;
   if (plan.bytes > 0) {
     char* ws = static_cast<char*>(workspace);
-    a.counters = plan.balanced
-                     ? reinterpret_cast<int32_t*>(ws + (workspace_bytes & ~int64_t{3}) - plan.counters_bytes)
-                     : nullptr;
+    a.counters = plan.balanced ? reinterpret_cast<int32_t*>(ws) : nullptr;
     a.part_ml = reinterpret_cast<float*>(ws + plan.ml_off);
     a.part_o = reinterpret_cast<float*>(ws + plan.o_off);
     a.unit_desc = plan.uniform ? reinterpret_cast<int32_t*>(ws + plan.desc_off) : nullptr;

@@ -1327,10 +1327,13 @@ __device__ __forceinline__ void merge_records(float* __restrict__ rec_ml, float*
 //   [floor(wC/W), floor((w+1)C/W)).  A unit cut by slice boundaries yields
 //   one piece per workgroup it touches; piece k of unit u writes a record at
 //   slot u + first_owner(u) + k (slots are distinct because both u and w only
-//   grow along the axis).  Records merge up a fan-in-kFanIn tree: a node's
-//   counter (ctr[level][slot of its first record]) counts finished children,
+//   grow along the axis).  Records merge up a fan-in-kFanIn tree: node k of a
+//   level counts its finished children in ctr[level][first_owner(u) + 1 + k],
 //   the last child to arrive merges them (or writes the output at the root)
-//   and resets the counter to zero for the next call.
+//   and resets the counter to zero for the next call.  A unit cut into n
+//   pieces holds the n − 1 slice boundaries first_owner + 1 … first_owner +
+//   n − 1 strictly inside it, no other unit holds them, and no level has more
+//   than n − 1 nodes, so the counters of different units are distinct.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int BS, int G, int NW>
 __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void decode_balanced_kernel(
@@ -1338,7 +1341,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
     void* __restrict__ out, int32_t out_dtype, int32_t* __restrict__ ctr, float* __restrict__ rec_ml,
     float* __restrict__ rec_o, const int32_t* __restrict__ block_tables, int32_t table_stride,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_blocks, int32_t kv_heads,
-    int32_t max_ctx, int32_t num_slots, float scale_log2) {
+    int32_t max_ctx, float scale_log2) {
   constexpr int NT = NW * 64;
   constexpr int CT = Chunk<DT, D, BS>::CT;
   // slices are cut at multiples of CT; the matrix-core loop reads 16-token tiles
@@ -1472,7 +1475,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
         const int32_t parent = idx / kFanIn;
         const int32_t nchild = min(kFanIn, n - parent * kFanIn);
         const int64_t pslot = slot0 + static_cast<int64_t>(parent) * kFanIn * span;
-        int32_t* counter = ctr + static_cast<int64_t>(level) * num_slots + pslot;
+        int32_t* counter = ctr + static_cast<int64_t>(level) * kCounterSlots + first_w + 1 + parent;
         wait_vmem();       // this wave's record stores have completed …
         __syncthreads();   // … and so have every other wave's
         if (tid == 0) sh_last = atomicAdd(counter, 1) == nchild - 1;
@@ -1741,8 +1744,7 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
     hipLaunchKernelGGL((decode_balanced_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
                        static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
                        a.out, a.out_dtype, a.counters, a.part_ml, a.part_o, a.block_tables, a.table_stride,
-                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.num_slots,
-                       a.scale_log2);
+                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.scale_log2);
     return hipGetLastError();
   }
   if (a.uniform) {

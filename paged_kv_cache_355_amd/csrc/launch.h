@@ -14,9 +14,17 @@ inline int32_t elem_bytes(int32_t dt) { return dt == kF32 ? 4 : 2; }
 // Largest grid of the balanced decode kernel (its merge tree holds at most
 // 16^3 records per unit, and a unit meets at most grid + 1 workgroups).
 constexpr int32_t kMaxBalancedGrid = 4095;
-// Levels of the balanced kernel's merge tree (one int32 counter per record
-// slot per level).
+// Levels of the balanced kernel's merge tree.
 constexpr int32_t kMergeLevels = 3;
+// Its merge counters: one int32 per slice boundary (0 … kMaxBalancedGrid) per
+// level.  A unit cut by the slices owns the boundaries strictly inside it, so
+// the counters of different units never meet, and their number does not
+// depend on the batch.  Every plan that uses a workspace reserves this region
+// at its front (zero-filled once; every balanced call leaves it zero) and puts
+// its partial records after it, so calls of any split mode can share one
+// workspace without writing over the counters.
+constexpr int32_t kCounterSlots = kMaxBalancedGrid + 1;
+constexpr int64_t kCounterBytes = int64_t{kMergeLevels} * kCounterSlots * 4;   // 48 KiB, a multiple of 256
 
 struct PoolDesc {
   int32_t num_blocks, block_size, kv_heads, head_dim, dtype;
@@ -40,7 +48,7 @@ struct DecodeArgs {
   bool balanced;
   int32_t grid;
   int32_t num_slots;       // num_seqs * kv_heads + grid
-  int32_t* counters;       // [kMergeLevels][num_slots], zero on entry and exit
+  int32_t* counters;       // [kMergeLevels][kCounterSlots], zero on entry and exit
   // Uniform split (uniform = true): `grid` workgroups, all resident at once;
   // the device picks one partition length that fits the batch's partitions
   // into them.  Partial records: [grid][group] rows; unit_desc[num_seqs ×

@@ -320,6 +320,33 @@ def test_balanced_workspace_reuse_leaves_counters_zero(gpu):
         assert np.max(np.abs(out_to_f64(out) - want[:n])) <= TOL["f16"]
 
 
+def test_one_workspace_serves_every_split_mode(gpu):
+    """One workspace, zero-filled once and sized to the largest split of the
+    batch, serves fixed partitions, the balanced split and the uniform split
+    in any order.  The fixed-partition plan needs the most bytes here, so its
+    records reach furthest into the workspace; the balanced calls that follow
+    must still find their merge counters at zero (PA_DEBUG_VALIDATE checks them
+    before each call) and every output matches the oracle."""
+    import torch
+    pk = gpu
+    case = build_case([2500, 17, 900, 1300, 64, 2047], 2, 4, 64, 16, "f16", 6, scale=1.0)
+    want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
+    pool = pk.Pool(case["num_blocks"], 16, 2, 64, "f16", k=to_torch(case["k_pool"], "f16"),
+                   v=to_torch(case["v_pool"], "f16"))
+    q, tables, lens = to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(), \
+        torch.from_numpy(case["lens"]).cuda()
+    bal, uni = pk.PA_PARTITION_BALANCED, pk.PA_PARTITION_UNIFORM
+    modes = [64, bal, uni, bal, 512, bal, uni, 16, bal]
+    sizes = {m: pk.decode_workspace_bytes(pool, 6, 8, 2500, m) for m in set(modes)}
+    assert sizes[16] == max(sizes.values()) > sizes[bal]   # the longest records reach past the balanced plan
+    ws = torch.zeros(max(sizes.values()), dtype=torch.uint8, device="cuda")
+    for m in modes:
+        out = pk.decode(pool, q, tables, lens, 2500, out_dtype="f32", workspace=ws, partition_tokens=m)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(out_to_f64(out) - want)) <= TOL["f16"], f"split {m}"
+    assert int(ws[:48 * 1024].count_nonzero()) == 0   # the counter region is back at zero
+
+
 def test_balanced_rejects_dirty_workspace_under_validation(gpu):
     import torch
     pk = gpu
@@ -328,7 +355,7 @@ def test_balanced_rejects_dirty_workspace_under_validation(gpu):
                    v=to_torch(case["v_pool"], "f16"))
     bal = pk.PA_PARTITION_BALANCED
     ws = torch.zeros(pk.decode_workspace_bytes(pool, 2, 1, 300, bal), dtype=torch.uint8, device="cuda")
-    ws[-1] = 1                                               # the merge counters sit at the end
+    ws[4] = 1                                                # the merge counters sit at the front
     with pytest.raises(pk.PaError) as e:
         pk.decode(pool, to_torch(case["q"], "f16"), torch.from_numpy(case["tables"]).cuda(),
                   torch.from_numpy(case["lens"]).cuda(), 300, workspace=ws, partition_tokens=bal)
