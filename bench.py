@@ -149,6 +149,40 @@ def split_meta(flat, B, stride):
             flat[t1:t1 + B + 1], flat[t1 + B + 1:t1 + 2 * B + 1])
 
 
+def prepare_run(pk, w, st, partition_arg=0, decode_arg="auto"):
+    """What the timed steps need besides the state: the split (the workload's
+    own unless partition_arg is not 0), whether the sharing-aware decode runs
+    (decode_arg "auto": when the batch has prefix groups), the device metadata
+    array with its views, a zero-filled decode workspace sized for the longest
+    context the steps reach, and the two pinned host buffers."""
+    import torch
+
+    B = st["B"]
+    part = w.partition_tokens if partition_arg == 0 else partition_arg
+    max_ctx_bound = st["stride"] * w.block_size
+    dev = {"flat": torch.empty(meta_len(B, st["stride"]), dtype=torch.int32, device="cuda")}
+    (dev["slots"], dev["lens"], dev["pairs"], dev["tables"], dev["group_start"],
+     dev["prefix"]) = split_meta(dev["flat"], B, st["stride"])
+    # the sharing-aware decode when the batch has prefix groups (and it was not turned off)
+    _, probe_prefix, _ = st["bm"].prefix_groups(st["ids"][st["bm"].dispatch_order(st["ids"])])
+    shared_prefix = decode_arg == "shared" or (decode_arg == "auto" and int(probe_prefix.max(initial=0)) > 0)
+    if shared_prefix and part < 0:
+        part = 0
+    if shared_prefix:
+        ws_bytes = pk.decode_shared_prefix_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound,
+                                                           max_ctx_bound, part)
+        resolved_part = part if part > 0 else (
+            -(-max_ctx_bound // w.block_size) * w.block_size
+            if pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, 0) > 0 else 512)
+    else:
+        ws_bytes = pk.decode_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
+        resolved_part = pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
+    dev["workspace"] = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")   # counters start at 0
+    hbufs = [HostBuffers(B, st["stride"]) for _ in range(2)]
+    return {"part": part, "shared_prefix": shared_prefix, "resolved_part": resolved_part, "dev": dev,
+            "hbufs": hbufs}
+
+
 # ----------------------------------------------------------------------------
 # the timed step
 # ----------------------------------------------------------------------------
@@ -356,23 +390,29 @@ def recorded_traffic(workload, decode):
     return rec.get("hbm_bytes_per_call"), round(rec["hbm_bytes_per_call"] / rec["algorithmic_bytes_per_call"], 4)
 
 
-def prefill_probe(pk, w, st, reps=5):
-    """Prompt admission at prompt scale: a fresh block manager over the first
-    layer's pool admits a second seeded draw of the workload's prompts
-    (add_seq, then each prompt's token slots), and one bulk pa_write_kv writes
-    every prompt token's K and V (partial last blocks included).  Runs after
-    the timed decode steps, whose pool contents it overwrites."""
+def prefill_admission(w, num_blocks):
+    """The prompts the prefill probe admits (a second seeded draw of the
+    workload's prompts, (seq id, tokens) in admission order) and the free-list
+    order of its fresh block manager."""
     import numpy as np
-    import torch
-    from paged_kv_cache_355_amd._lib import lib, check
-    from workloads import make_scenario, device_fill_, seed_for
+    from workloads import make_scenario, seed_for
 
-    pool = st["pools"][0]
     sc2 = make_scenario(w, repetition=1)
     prompts = [(op[1], op[2]) for op in sc2.setup if op[0] == "add"]
-    seed = seed_for(w, 1)
-    bm = pk.BlockManager(pool.num_blocks, w.block_size, np.random.default_rng(seed).permutation(pool.num_blocks))
+    return prompts, np.random.default_rng(seed_for(w, 1)).permutation(num_blocks)
+
+
+def prefill_inputs(pk, w, pool):
+    """A fresh block manager over ``pool`` admits the prefill prompts until the
+    pool is full (add_seq, then each prompt's token slots); returns the slots
+    of every admitted prompt token and seeded K/V rows for them on the device."""
+    import numpy as np
+    import torch
+    from workloads import device_fill_, seed_for
+
+    prompts, order = prefill_admission(w, pool.num_blocks)
     t0 = time.perf_counter()
+    bm = pk.BlockManager(pool.num_blocks, w.block_size, order)
     slots = []
     admitted = 0
     for sid, n in prompts:
@@ -385,11 +425,29 @@ def prefill_probe(pk, w, st, reps=5):
     slots = np.concatenate(slots).astype(np.int32)
     host_ms = (time.perf_counter() - t0) * 1e3
     n_tok = int(slots.shape[0])
+    seed = seed_for(w, 1)
     tdt = pk.torch_dtype(w.dtype)
     k_new = device_fill_(torch.empty((n_tok, w.kv_heads, w.head_dim), dtype=tdt, device="cuda"), seed + 11,
                          w.value_scale)
     v_new = device_fill_(torch.empty_like(k_new), seed + 12, w.value_scale)
-    slots_dev = torch.from_numpy(slots).cuda()
+    return {"bm": bm, "admitted": admitted, "slots": slots, "slots_dev": torch.from_numpy(slots).cuda(),
+            "k_new": k_new, "v_new": v_new, "host_admit_ms": host_ms}
+
+
+def prefill_probe(pk, w, st, reps=5):
+    """Prompt admission at prompt scale: a fresh block manager over the first
+    layer's pool admits a second seeded draw of the workload's prompts
+    (add_seq, then each prompt's token slots), and one bulk pa_write_kv writes
+    every prompt token's K and V (partial last blocks included).  Runs after
+    the timed decode steps, whose pool contents it overwrites."""
+    import torch
+    from paged_kv_cache_355_amd._lib import lib, check
+
+    pool = st["pools"][0]
+    pre = prefill_inputs(pk, w, pool)
+    host_ms = pre["host_admit_ms"]
+    admitted, k_new, v_new, slots_dev = pre["admitted"], pre["k_new"], pre["v_new"], pre["slots_dev"]
+    n_tok = int(pre["slots"].shape[0])
     stream = torch.cuda.current_stream()
     L = lib()
     args = (pool.handle, k_new.data_ptr(), v_new.data_ptr(), slots_dev.data_ptr(), n_tok, stream.cuda_stream)
@@ -548,27 +606,10 @@ def main():
         f"{w.dtype} bs={w.block_size} pool={sc.num_blocks} blocks x {args.layers} layers")
     st = build_state(pk, w, sc, args.layers, steps_total)
     B = st["B"]
-    part = w.partition_tokens if args.partition_tokens == 0 else args.partition_tokens
+    run = prepare_run(pk, w, st, args.partition_tokens, args.decode)
+    part, shared_prefix, resolved_part = run["part"], run["shared_prefix"], run["resolved_part"]
+    dev, hbufs = run["dev"], run["hbufs"]
     max_ctx_bound = st["stride"] * w.block_size
-    dev = {"flat": torch.empty(meta_len(B, st["stride"]), dtype=torch.int32, device="cuda")}
-    (dev["slots"], dev["lens"], dev["pairs"], dev["tables"], dev["group_start"],
-     dev["prefix"]) = split_meta(dev["flat"], B, st["stride"])
-    # the sharing-aware decode when the batch has prefix groups (and it was not turned off)
-    _, probe_prefix, _ = st["bm"].prefix_groups(st["ids"][st["bm"].dispatch_order(st["ids"])])
-    shared_prefix = args.decode == "shared" or (args.decode == "auto" and int(probe_prefix.max(initial=0)) > 0)
-    if shared_prefix and part < 0:
-        part = 0
-    if shared_prefix:
-        ws_bytes = pk.decode_shared_prefix_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound,
-                                                           max_ctx_bound, part)
-        resolved_part = part if part > 0 else (
-            -(-max_ctx_bound // w.block_size) * w.block_size
-            if pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, 0) > 0 else 512)
-    else:
-        ws_bytes = pk.decode_workspace_bytes(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
-        resolved_part = pk.decode_partition_tokens(st["pools"][0], B, w.q_heads, max_ctx_bound, part)
-    dev["workspace"] = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")   # counters start at 0
-    hbufs = [HostBuffers(B, st["stride"]) for _ in range(2)]
     torch.cuda.synchronize()
     log(f"[bench] state ready; warmup {args.warmup} steps")
 
