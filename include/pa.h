@@ -230,6 +230,26 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
                     int32_t max_context_len, float scale, int32_t partition_tokens,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/* pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * arguments and the result are pa_decode's without the workspace: partial
+ * results go to a device array that the library holds for each GPU it runs on
+ * (16 MiB, kept until the process ends; its address is looked up on the first
+ * call on a device).  Nothing is allocated, by this call or any other.
+ *   - Splits whose partial results need more than 16 MiB (pa_decode_workspace
+ *     _bytes above 16777216) are rejected with PA_ERR_INVALID before
+ *     anything is enqueued.
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     there.  Before a balanced split the call clears the merge counters with
+ *     a fill kernel on `stream` (no memset).  Calls that may overlap on one
+ *     GPU (other streams, other threads) race on the array: serialise them.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
+pa_status pa_decode_noalloc(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q,
+                            int32_t num_seqs, int32_t q_heads, const int32_t* block_tables,
+                            int32_t block_table_stride, const int32_t* context_lens,
+                            int32_t max_context_len, float scale, int32_t partition_tokens,
+                            void* stream);
+
 /* One decode step's KV write and attention in one launch ([P2] §3.2.2: step 3
  * writes the new token's K/V into its slot, step 4 attends over every cached
  * token, the new one included).  The result — pool contents and out — is that

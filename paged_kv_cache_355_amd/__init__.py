@@ -7,10 +7,10 @@ falls back to another implementation.
 """
 from ._lib import PaError, NoBlocksError, LIB_PATH, lib, PA_PARTITION_BALANCED, PA_PARTITION_UNIFORM
 from .api import (Pool, BlockManager, write_kv, copy_blocks, swap_out, swap_in, decode, decode_workspace_bytes,
-                  decode_partition_tokens, decode_shared_prefix, decode_shared_prefix_workspace_bytes, torch_dtype,
-                  dtype_name)
+                  decode_partition_tokens, decode_noalloc, decode_shared_prefix,
+                  decode_shared_prefix_workspace_bytes, torch_dtype, dtype_name)
 
 __all__ = ["PaError", "NoBlocksError", "LIB_PATH", "lib", "PA_PARTITION_BALANCED", "PA_PARTITION_UNIFORM", "Pool",
            "BlockManager", "write_kv", "copy_blocks", "swap_out", "swap_in", "decode", "decode_workspace_bytes",
-           "decode_partition_tokens", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes", "torch_dtype",
-           "dtype_name"]
+           "decode_partition_tokens", "decode_noalloc", "decode_shared_prefix",
+           "decode_shared_prefix_workspace_bytes", "torch_dtype", "dtype_name"]

@@ -53,6 +53,8 @@ SIGNATURES = {
     "pa_decode_partition_tokens": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_p]),
     "pa_decode": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_i32, c_p, c_i32, c_p, c_i32, ctypes.c_float, c_i32,
                           c_p, c_i64, c_p]),
+    "pa_decode_noalloc": (c_i32, [c_p, c_p, c_i32, c_p, c_i32, c_i32, c_p, c_i32, c_p, c_i32, ctypes.c_float, c_i32,
+                                  c_p]),
     "pa_decode_append": (c_i32, [c_p, c_p, c_p, c_p, c_p, c_i32, c_p, c_i32, c_i32, c_p, c_i32, c_p, c_i32,
                                  ctypes.c_float, c_i32, c_p, c_i64, c_p]),
     "pa_decode_shared_prefix_workspace_bytes": (c_i32, [c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_p]),

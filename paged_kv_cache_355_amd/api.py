@@ -179,6 +179,28 @@ def decode(pool, q, block_tables, context_lens, max_context_len, out=None, out_d
     return out
 
 
+def decode_noalloc(pool, q, block_tables, context_lens, max_context_len, out=None, out_dtype=None, scale=None,
+                   partition_tokens=0, stream=None):
+    """``decode`` without a workspace (pa_decode_noalloc): partial results go
+    to the library's static per-GPU array; ``out`` is the only buffer used.
+    Calls that may overlap on one GPU must be serialised."""
+    import torch
+    num_seqs, q_heads, d = (int(x) for x in q.shape)
+    if d != pool.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    odt = out_dtype or pool.dtype
+    if out is None:
+        out = torch.empty((num_seqs, q_heads, d), dtype=torch_dtype(odt), device=q.device)
+    stride = int(block_tables.shape[1]) if block_tables.dim() == 2 else 0
+    check(lib().pa_decode_noalloc(
+        pool.handle, _dev_ptr(out, "out", torch_dtype(odt), (num_seqs, q_heads, d)), DTYPE_CODES[odt],
+        _dev_ptr(q, "q", torch_dtype(pool.dtype)), num_seqs, q_heads,
+        _dev_ptr(block_tables, "block_tables", torch.int32), stride,
+        _dev_ptr(context_lens, "context_lens", torch.int32, (num_seqs,)), int(max_context_len),
+        float(scale) if scale else 0.0, int(partition_tokens), _stream(stream)), "pa_decode_noalloc")
+    return out
+
+
 def decode_shared_prefix_workspace_bytes(pool, num_seqs, q_heads, max_context_len, max_prefix_tokens,
                                          partition_tokens=0):
     """Workspace bytes ``decode_shared_prefix`` needs."""

@@ -27,6 +27,7 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "
 
 SOURCES = [
     ("kv_kernels.hip", True),
+    ("scratch.hip", True),
     ("decode_f32.hip", True),
     ("decode_f16.hip", True),
     ("decode_bf16.hip", True),

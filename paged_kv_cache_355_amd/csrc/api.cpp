@@ -540,6 +540,40 @@ pa_status pa_decode(const pa_pool* pool, void* out, pa_dtype out_dtype, const vo
                      stream);
 }
 
+pa_status pa_decode_noalloc(const pa_pool* pool, void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs,
+                            int32_t q_heads, const int32_t* block_tables, int32_t block_table_stride,
+                            const int32_t* context_lens, int32_t max_context_len, float scale,
+                            int32_t partition_tokens, void* stream) {
+  if (!pool) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PA_ERR_INVALID, "num_seqs must be in [0, 65535]");
+  if (num_seqs == 0) return PA_OK;
+  if (q_heads <= 0 || q_heads % pool->d.kv_heads != 0)
+    return fail(PA_ERR_INVALID, "q_heads must be a positive multiple of kv_heads");
+  if (max_context_len < 0) return fail(PA_ERR_INVALID, "max_context_len must be >= 0");
+  DecodePlan plan;
+  if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
+  if (plan.bytes > pa::kScratchBytes)
+    return fail(PA_ERR_INVALID, "this split keeps " + std::to_string(plan.bytes) +
+                                    " bytes of partial results; pa_decode_noalloc holds " +
+                                    std::to_string(pa::kScratchBytes) +
+                                    " (pass pa_decode a workspace, or choose fewer partitions)");
+  void* ws = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.bytes > 0) {
+    hipError_t e = pa::scratch_buffer(&ws);
+    if (e != hipSuccess) return hip_fail(e, "static workspace address");
+    // the array keeps the previous call's contents: the balanced split's
+    // merge counters must start at zero
+    if (plan.balanced) {
+      e = pa::launch_zero(ws, pa::kCounterBytes, st);
+      if (e != hipSuccess) return hip_fail(e, "zero the merge counters");
+    }
+  }
+  return decode_call(pool, out, out_dtype, q, num_seqs, q_heads, block_tables, block_table_stride, context_lens,
+                     max_context_len, scale, partition_tokens, ws, ws ? pa::kScratchBytes : 0, nullptr, nullptr,
+                     nullptr, stream);
+}
+
 pa_status pa_decode_append(pa_pool* pool, const void* k_new, const void* v_new, const int32_t* slot_mapping,
                            void* out, pa_dtype out_dtype, const void* q, int32_t num_seqs, int32_t q_heads,
                            const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,

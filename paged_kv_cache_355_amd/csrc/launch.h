@@ -80,6 +80,17 @@ struct DecodeArgs {
   const int32_t* kv_slots = nullptr;
 };
 
+// The library-held workspace of pa_decode_noalloc: one array of this many
+// bytes per GPU (a file-scope device array in scratch.hip).
+constexpr int64_t kScratchBytes = int64_t{16} << 20;
+
+// Device address of that array on the current device, looked up once per
+// device (hipGetSymbolAddress) and cached.
+hipError_t scratch_buffer(void** ptr);
+// Zero `bytes` (a multiple of 16) at p with a fill kernel on stream (no
+// memset node, so the call can be captured into a graph).
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t stream);
+
 // True when the shared-prefix kernels exist for this pool (16-bit K/V, blocks
 // of at least 16 tokens: the matrix-core tile).
 inline bool shared_prefix_supported(int32_t dtype, int32_t block_size) {
