@@ -8,8 +8,10 @@ attention layer of a model slice:
    block tables and lengths, written into pinned host memory);
 2. the metadata goes to the device (async copies on the stream);
 3. per layer: ``pa_copy_blocks`` (if the step made copy-on-write pairs),
-   ``pa_write_kv`` of the new token's K/V, ``pa_decode`` over every cached
-   token.
+   then one ``pa_decode_append`` call that writes the new token's K/V into
+   its slot and attends over every cached token (``--separate-write``:
+   ``pa_write_kv`` then ``pa_decode``).  A batch with prefix groups takes
+   ``pa_write_kv`` then ``pa_decode_shared_prefix``.
 
 Each layer has its own KV pool (same block tables, as in a model), so
 consecutive decodes never re-read KV that the previous one left in the
@@ -66,9 +68,9 @@ def parse_args():
     ap.add_argument("--timed-layers", choices=["one", "all"], default="one",
                     help="decode calls bracketed by HIP events: one layer's per step, rotating (default), "
                          "or every layer's")
-    ap.add_argument("--fused-append", action="store_true",
-                    help="one pa_decode_append call per layer (KV write inside the decode launch) instead of "
-                         "pa_write_kv then pa_decode")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="pa_write_kv then pa_decode per layer, instead of one pa_decode_append call (the KV write "
+                         "inside the decode launch; the default wherever the batch has no prefix groups)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-admission (bulk pa_write_kv) probe")
     ap.add_argument("--no-swap", action="store_true", help="skip the block swap (pa_swap_out / pa_swap_in) probe")
@@ -613,7 +615,8 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] state ready; warmup {args.warmup} steps")
 
-    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None, shared_prefix, args.fused_append)
+    fused_append = not args.separate_write
+    run_steps(pk, w, st, args.warmup, part, dev, hbufs, 0, None, shared_prefix, fused_append)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     # HIP events around one layer's decode call per step, the layer rotating
@@ -625,7 +628,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     kv_bytes = run_steps(pk, w, st, args.steps, part, dev, hbufs, args.warmup, timing, shared_prefix,
-                         args.fused_append)
+                         fused_append)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     dec_ms = [a.elapsed_time(b) for a, b in timing["used"]]
@@ -640,7 +643,7 @@ def main():
     mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
     achieved = per_call_bytes / mean_dec_s / 1e9
     value = total_kv / elapsed / 1e9
-    entry = "pa_decode_shared_prefix" if shared_prefix else ("pa_decode_append" if args.fused_append else "pa_decode")
+    entry = "pa_decode_shared_prefix" if shared_prefix else ("pa_decode_append" if fused_append else "pa_decode")
     traffic, traffic_ratio = recorded_traffic(w.name, entry)
     dec_sorted = sorted(dec_ms)
     result = {
@@ -689,8 +692,13 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
+            # HBM bytes per call of this run: the ratio that the committed
+            # FETCH_SIZE/WRITE_SIZE runs measured for this kernel source and
+            # entry point, times this run's algorithmic bytes per call
+            "traffic": None if traffic_ratio is None else int(round(traffic_ratio * per_call_bytes)),
             "traffic_over_algorithmic": traffic_ratio,
+            "traffic_source": None if traffic_ratio is None else
+            f"profiles/decode_{w.name}_traffic.txt (counted {traffic} B per call on shorter contexts)",
             "algorithmic_bytes_per_call": int(per_call_bytes),
         },
         "cpu_baseline": None,

@@ -264,10 +264,12 @@ pa_status pa_decode_noalloc(const pa_pool* pool, void* out, pa_dtype out_dtype, 
  *     returns.  Live slots are distinct.  A slot outside the pool is skipped.
  *   The remaining arguments are pa_decode's, with its workspace rules.
  * The workgroup that attends over the last token of (sequence, kv-head)
- * writes that row first and reads it back after a barrier, so no second
- * launch is needed.  The balanced split (PA_PARTITION_BALANCED) has no single
- * owner of the last token: there the library enqueues pa_write_kv's kernel
- * before the decode.  A slot that is not the last token's gives undefined
+ * takes that token's K and V rows from k_new/v_new (staged in LDS with its
+ * first block ids) in place of its slot, and stores them into the slot after
+ * its token loop, so neither a second launch nor a wait for the store is
+ * needed; the values are the same bytes, so the result is unchanged.  The
+ * balanced split (PA_PARTITION_BALANCED) has no single owner of the last
+ * token: there the library enqueues pa_write_kv's kernel before the decode.  A slot that is not the last token's gives undefined
  * rows (never an access outside the pool); PA_DEBUG_VALIDATE=1 checks the
  * slots against the tables and lengths on the host.
  * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */

@@ -220,6 +220,11 @@ constexpr bool kUseMfma = DT != kF32 && BS >= 16 && G >= 4;
 // accumulators then stay in VGPRs; otherwise what the register file allows.
 template <int DT, int BS, int G, bool BALANCED>
 constexpr int kMinWavesPerEU = kUseMfma<DT, BS, G> ? (BALANCED ? 1 : 3) : (G <= (BALANCED ? 1 : 2) ? 4 : 1);
+// Kernels that keep more state live around the loop (the append kernels'
+// new-token row, the uniform kernel's task): with two query rows the vector
+// loop then spills at 4 waves, so it is compiled for 3.
+template <int DT, int BS, int G, bool EXTRA>
+constexpr int kMinWavesExtra = (EXTRA && !kUseMfma<DT, BS, G> && G == 2) ? 3 : kMinWavesPerEU<DT, BS, G, false>;
 
 template <int NW, int G, int D, bool MFMA>
 struct WaveMerge {
@@ -239,6 +244,7 @@ struct WaveMerge {
   float l[NW][G];
   int bad[NW];
   int32_t tbl[kTableBatch];   // physical block ids, -1 for an id outside the pool
+  uint4 newrow[2][D / 4];     // pa_decode_append: the new token's K and V rows (≤ 4-byte elements)
 };
 
 // A 16-byte K/V load.  STREAM selects the non-temporal (streaming) cache
@@ -323,6 +329,32 @@ __device__ __forceinline__ uint16_t round16(float x, float* back) {
   }
 }
 
+// The new token of pa_decode_append, as the workgroup that attends over it
+// sees it: t is its index in the sequence (-1: none here), k and v the starts
+// of its K and V rows for this kv-head in k_new / v_new.  The workgroup copies
+// the two rows into LDS with its first block ids and uses them in place of
+// what its chunk loads fetched from the slot, which it writes only after its
+// token loop (the same bytes, so the result is the same).
+struct NewToken {
+  const char* k = nullptr;
+  const char* v = nullptr;
+  int32_t t = -1;
+};
+
+// Copy the new token's K and V rows (ROW bytes each) into LDS; called by every
+// thread of the workgroup before the barrier that publishes the block ids, so
+// the loads overlap the table loads.
+template <int ROW, int N>
+__device__ __forceinline__ void stage_new_token(const NewToken& nt, uint4 (&newrow)[2][N]) {
+  constexpr int L16 = ROW / 16;
+  static_assert(L16 <= N, "row buffer too small");
+  if (nt.t >= 0 && threadIdx.x < 2 * L16) {
+    const bool is_v = threadIdx.x >= L16;
+    const int piece = threadIdx.x % L16;
+    newrow[is_v ? 1 : 0][piece] = *reinterpret_cast<const uint4*>((is_v ? nt.v : nt.k) + piece * 16);
+  }
+}
+
 // Whether sequence s shares its first physical block with a batch neighbour
 // (s − 1 or s + 1), i.e. reads a prefix that a sibling scheduled next to it
 // also reads.  Rows of empty sequences may hold anything; a false match only
@@ -340,12 +372,13 @@ __device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ b
 // t_end).  q_lane: the start of this lane's query row (row lane % 16), or
 // nullptr for a row past R or unused (it contributes zeros); q_dummy: any
 // valid, cache-resident address (read by the loads of chunks past the end).
-template <int DT, int D, int BS, int R, int NW, bool STREAM, typename Emit>
+template <int DT, int D, int BS, int R, int NW, bool STREAM, bool NEWTOK, typename Emit>
 __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
                                                   const char* q_lane, const char* __restrict__ q_dummy,
                                                   const int32_t* __restrict__ table, int32_t g, int32_t kv_heads,
                                                   int32_t num_blocks, int32_t t_begin, int32_t t_end,
-                                                  float scale_log2, WaveMerge<NW, R, D, true>& sh, Emit&& emit) {
+                                                  float scale_log2, NewToken nt, WaveMerge<NW, R, D, true>& sh,
+                                                  Emit&& emit) {
   constexpr int EB = 2;
   constexpr int ROW = D * EB;          // bytes per token row
   constexpr int CT = 16;               // tokens per chunk (the MFMA M dimension)
@@ -363,8 +396,11 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   const int qd = lane >> 4;   // quarter: dim slice of the loads, token group of S/P
 
   // Qᵀ operand: row tl (zero where q_lane is null), dims [32i + 8qd, +8)
-  const char* q_row = q_dummy + qd * 16;   // dead loads read here
   const char* q_src = (q_lane ? q_lane : q_dummy) + qd * 16;
+  // dead loads read here: the same 16 bytes for every lane with the new-token
+  // path (one pointer fewer), this lane's slice of q otherwise (either fits
+  // the 3-wave register budget only that way)
+  const char* q_dead = NEWTOK ? q_dummy : q_src;
   uint4 qop[NKL];
 #pragma unroll
   for (int i = 0; i < NKL; ++i) {
@@ -388,15 +424,17 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       const int32_t phys = table[bb + i];
       sh.tbl[i] = static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks) ? phys : -1;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): an append_token store is in L2 before the barrier
+    if constexpr (NEWTOK) {
+      if (bb == blk_first) stage_new_token<ROW>(nt, sh.newrow);
+    }
     __syncthreads();
     const int32_t tb = max(t_begin, bb * BS);
     const int32_t te = min(t_end, (bb + nb) * BS);
     const int32_t nchunks = (te - tb + CT - 1) / CT;
 
-    // Issue chunk c's K and V loads (live = false: read q instead, which is
-    // valid and cache-resident).  Rows past te inside the block may be read;
-    // they are masked before use.
+    // Issue chunk c's K and V loads (live = false: read q_dead, valid and
+    // cache-resident).  Rows past te inside the block may be read; they are
+    // masked before use.
     auto load_chunk = [&](int32_t c, bool live, uint4 (&kb)[NKL], uint4 (&vb)[NKL]) {
       const int32_t tok0 = tb + (live ? c : 0) * CT;
       int32_t phys = sh.tbl[tok0 / BS - bb];
@@ -407,13 +445,25 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       const int64_t tile = (static_cast<int64_t>(phys) * kv_heads + g) * TILE + (tok0 % BS) * ROW;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        kb[i] = load_kv<STREAM>(live ? k_pool + tile + v_off + i * RPI * ROW : q_row);
-        vb[i] = load_kv<STREAM>(live ? v_pool + tile + v_off + i * RPI * ROW : q_row);
+        kb[i] = load_kv<STREAM>(live ? k_pool + tile + v_off + i * RPI * ROW : q_dead);
+        vb[i] = load_kv<STREAM>(live ? v_pool + tile + v_off + i * RPI * ROW : q_dead);
       }
     };
 
-    auto consume_chunk = [&](int32_t c, const uint4 (&kb)[NKL], const uint4 (&vb)[NKL]) {
+    auto consume_chunk = [&](int32_t c, uint4 (&kb)[NKL], uint4 (&vb)[NKL]) {
       const int32_t tok0 = tb + c * CT;
+      if constexpr (NEWTOK) {
+        // the new token's row (its slot is written after the loop) from LDS
+        if (nt.t >= tok0 && nt.t < tok0 + CT) {   // wave-uniform
+#pragma unroll
+          for (int i = 0; i < NKL; ++i) {
+            if (tok0 + i * RPI + vrow == nt.t) {
+              kb[i] = sh.newrow[0][lane % LPR];
+              vb[i] = sh.newrow[1][lane % LPR];
+            }
+          }
+        }
+      }
       // K rows into the wave's K tile, then read back in the A layout
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
@@ -572,18 +622,20 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 // Block ids come from LDS, staged kTableBatch at a time, so no global load of
 // the table sits between two chunks.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int BS, int G, int NW, bool STREAM, typename Emit>
+template <int DT, int D, int BS, int G, int NW, bool STREAM, bool NEWTOK, typename Emit>
 __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, const char* __restrict__ v_pool,
                                              const char* __restrict__ q, const int32_t* __restrict__ table,
                                              int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
-                                             int32_t t_begin, int32_t t_end, float scale_log2,
+                                             int32_t t_begin, int32_t t_end, float scale_log2, NewToken nt,
                                              WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
   if constexpr (kUseMfma<DT, BS, G>) {
     constexpr int EB = 2;
     const int tl = threadIdx.x & 15;
     const char* q_head0 = q + ((static_cast<int64_t>(s) * kv_heads * G + g * G) * D) * EB;   // row g·G of sequence s
-    attend_range_mfma<DT, D, BS, G, NW, STREAM>(k_pool, v_pool, tl < G ? q_head0 + tl * D * EB : nullptr, q_head0,
-                                                table, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh, emit);
+    attend_range_mfma<DT, D, BS, G, NW, STREAM, NEWTOK>(k_pool, v_pool, tl < G ? q_head0 + tl * D * EB : nullptr,
+                                                        q_head0,
+                                                table, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, sh,
+                                                emit);
     return;
   } else {
   using S = Shape<DT, D>;
@@ -627,7 +679,9 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
       const int32_t phys = table[bb + i];
       sh.tbl[i] = static_cast<uint32_t>(phys) < static_cast<uint32_t>(num_blocks) ? phys : -1;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): an append_token store is in L2 before the barrier
+    if constexpr (NEWTOK) {
+      if (bb == blk_first) stage_new_token<ROW>(nt, sh.newrow);
+    }
     __syncthreads();
     const int32_t tb = max(t_begin, bb * BS);
     const int32_t te = min(t_end, (bb + nb) * BS);
@@ -679,9 +733,23 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
     };
 
     // Fold chunk c into the running (m, l, o) of this lane group.
-    auto consume_chunk = [&](int32_t c, const uint4 (&kb)[NLC], const uint4 (&vb)[NLC]) {
+    auto consume_chunk = [&](int32_t c, uint4 (&kb)[NLC], uint4 (&vb)[NLC]) {
       const int32_t tok0 = tb + c * CT;
       const bool full = tok0 + CT <= te;   // wave-uniform
+      if constexpr (NEWTOK) {
+        // the new token's row (its slot is written after the loop) from LDS:
+        // it sits in load i_new (wave-uniform), in the lanes of group g_new
+        if (nt.t >= tok0 && nt.t < tok0 + CT) {   // wave-uniform
+          const int32_t i_new = (nt.t - tok0) / TPL, g_new = (nt.t - tok0) % TPL;
+#pragma unroll
+          for (int i = 0; i < NLC; ++i) {
+            if (i == i_new && grp == g_new) {
+              kb[i] = sh.newrow[0][sub];
+              vb[i] = sh.newrow[1][sub];
+            }
+          }
+        }
+      }
       bool valid[NLC];
 #pragma unroll
       for (int i = 0; i < NLC; ++i) valid[i] = full || (tok0 + grp + i * TPL < te);
@@ -847,19 +915,14 @@ __device__ __forceinline__ void fill_rows(void* out, int32_t out_dtype, int32_t 
   for (int32_t i = threadIdx.x; i < n; i += blockDim.x) store_out(out, out_dtype, first + i, value);
 }
 
-// attend_range with the cache policy chosen at run time (wave-uniform): the
-// streaming policy unless the tiles are shared with a neighbouring sequence.
 // The KV write of pa_decode_append ([P2] §3.2.2 step 3, then step 4 in the
 // same launch): the workgroup whose range ends at the context's last token
 // stores that token's K and V rows of kv-head g, k_new/v_new[s][g][:], into
 // slot kv_slots[s] (skipped when the slot is −1 or outside the pool), exactly
-// as write_kv_kernel would.  attend_range waits for every wave's outstanding
-// memory operations (vmcnt(0)) before the barrier that publishes the block
-// ids, which its table loads need anyway; that barrier then orders the stores
-// before every K/V load of the workgroup, so the token is read back from the
-// pool like any other, and the store's round trip overlaps the table loads.
-// The slot must hold token len−1 of sequence s; only this workgroup reads that
-// (block, kv-head) tile, because partitions start on block boundaries.
+// as write_kv_kernel would.  It stores them after its token loop and waits for
+// nothing: its own loads of that token read k_new/v_new (new_token_of), and no
+// other workgroup reads the slot, because partitions start on block
+// boundaries and the slot must hold token len−1 of sequence s.
 template <int DT, int D, int BS>
 __device__ __forceinline__ void append_token(const char* k_pool, const char* v_pool, const char* __restrict__ k_new,
                                              const char* __restrict__ v_new, const int32_t* __restrict__ kv_slots,
@@ -878,19 +941,40 @@ __device__ __forceinline__ void append_token(const char* k_pool, const char* v_p
   *reinterpret_cast<uint4*>(const_cast<char*>(is_v ? v_pool : k_pool) + dst) = v;
 }
 
-template <int DT, int D, int BS, int G, int NW, typename Emit>
+// The new token as the workgroup that owns token len−1 of (s, g) reads it:
+// from k_new/v_new when append_token will write it into the pool (a valid
+// slot), else none (then the pool already holds it).
+template <int DT, int D, int BS>
+__device__ __forceinline__ NewToken new_token_of(const char* __restrict__ k_new, const char* __restrict__ v_new,
+                                                 const int32_t* __restrict__ kv_slots, int32_t s, int32_t g,
+                                                 int32_t kv_heads, int32_t num_blocks, int32_t len) {
+  NewToken nt;
+  if (!kv_slots || len <= 0) return nt;
+  const int32_t slot = kv_slots[s];
+  if (slot < 0 || static_cast<int64_t>(slot) >= static_cast<int64_t>(num_blocks) * BS) return nt;
+  constexpr int ROW = D * Elem<DT>::bytes;
+  const int64_t off = (static_cast<int64_t>(s) * kv_heads + g) * ROW;
+  nt.k = k_new + off;
+  nt.v = v_new + off;
+  nt.t = len - 1;
+  return nt;
+}
+
+// attend_range with the cache policy chosen at run time (wave-uniform): the
+// streaming policy unless the tiles are shared with a neighbouring sequence.
+template <int DT, int D, int BS, int G, int NW, bool NEWTOK, typename Emit>
 __device__ __forceinline__ void attend_range_policy(bool shared, const char* __restrict__ k_pool,
                                                     const char* __restrict__ v_pool, const char* __restrict__ q,
                                                     const int32_t* __restrict__ table, int32_t s, int32_t g,
                                                     int32_t kv_heads, int32_t num_blocks, int32_t t_begin,
-                                                    int32_t t_end, float scale_log2,
+                                                    int32_t t_end, float scale_log2, NewToken nt,
                                                     WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
   if (shared) {
-    attend_range<DT, D, BS, G, NW, false>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
-                                          scale_log2, sh, emit);
+    attend_range<DT, D, BS, G, NW, false, NEWTOK>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin,
+                                                  t_end, scale_log2, nt, sh, emit);
   } else {
-    attend_range<DT, D, BS, G, NW, true>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end,
-                                         scale_log2, sh, emit);
+    attend_range<DT, D, BS, G, NW, true, NEWTOK>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin,
+                                                 t_end, scale_log2, nt, sh, emit);
   }
 }
 
@@ -906,8 +990,8 @@ __device__ __forceinline__ void attend_range_policy(bool shared, const char* __r
 //   partition and kv_heads a multiple of 8, kv-head g of every sequence lands
 //   on XCD g mod 8 and adjacent siblings find their shared tiles in its L2.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void decode_partition_kernel(
+template <int DT, int D, int BS, int G, int NW, bool APPEND>
+__global__ __launch_bounds__(NW * 64, (kMinWavesExtra<DT, BS, G, APPEND>)) void decode_partition_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
@@ -923,10 +1007,12 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   const bool bad_len = len < 0 || len > max_ctx;
   const int32_t len_c = bad_len ? 0 : len;
   // pa_decode_append (no shared prefix there): the last partition owns the
-  // new token; an empty or invalid context's only workgroup still writes it
-  if (kv_slots && p == max(parts_of(len_c, part_tokens), 1) - 1)
-    append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
+  // new token.  An empty or invalid context's only workgroup writes it at
+  // once; otherwise the owner reads it from k_new/v_new and writes it into
+  // the pool after its token loop.
+  const bool owner = APPEND && p == max(parts_of(len_c, part_tokens), 1) - 1;
   if (len_c == 0) {
+    if (owner) append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
     if (p == 0) fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
     return;
   }
@@ -954,8 +1040,10 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
   // after a prefix pass the tiles read here are this sequence's own
   const bool shared = pre == 0 && shares_first_block(block_tables, table_stride, s, num_seqs);
-  attend_range_policy<DT, D, BS, G, NW>(
-      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
+  const NewToken nt =
+      owner ? new_token_of<DT, D, BS>(k_new, v_new, kv_slots, s, g, kv_heads, num_blocks, len_c) : NewToken{};
+  attend_range_policy<DT, D, BS, G, NW, APPEND>(
+      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
         if (nsp == 1) {
@@ -970,6 +1058,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
           }
         }
       });
+  if (owner) append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
 }
 
 // ---------------------------------------------------------------------------
@@ -1032,11 +1121,11 @@ __global__ __launch_bounds__(NW * 64, 3) void decode_prefix_kernel(
     }
   };
   if (m_end - m_begin <= MT) {
-    attend_range_mfma<DT, D, BS, 16, NW, true>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
-                                               t_begin, t_end, scale_log2, sh, emit);
+    attend_range_mfma<DT, D, BS, 16, NW, true, false>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
+                                               t_begin, t_end, scale_log2, NewToken{}, sh, emit);
   } else {
-    attend_range_mfma<DT, D, BS, 16, NW, false>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
-                                                t_begin, t_end, scale_log2, sh, emit);
+    attend_range_mfma<DT, D, BS, 16, NW, false, false>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
+                                                t_begin, t_end, scale_log2, NewToken{}, sh, emit);
   }
 }
 
@@ -1453,8 +1542,8 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
       int32_t n = static_cast<int32_t>(slice_owner(off + c - 1, C, W) - first_w + 1);   // pieces
       int32_t idx = static_cast<int32_t>(w - first_w);
       const int64_t my_slot = slot0 + idx;
-      attend_range_policy<DT, D, BS, G, NW>(
-          shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, sh,
+      attend_range_policy<DT, D, BS, G, NW, false>(
+          shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, NewToken{}, sh,
           [&](int r, int d, float M, float L, float O, bool bad) {
             if (whole) {
               const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
@@ -1625,8 +1714,8 @@ __device__ bool uniform_task(const int32_t* __restrict__ lens, int32_t num_seqs,
 //   t·G … t·G+G−1) and, from partition 0, (t0, n) into unit_desc[unit] for
 //   decode_reduce_kernel.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void decode_uniform_kernel(
+template <int DT, int D, int BS, int G, int NW, bool APPEND>
+__global__ __launch_bounds__(NW * 64, (kMinWavesExtra<DT, BS, G, true>)) void decode_uniform_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const char* __restrict__ q,
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t* __restrict__ unit_desc, const int32_t* __restrict__ block_tables, int32_t table_stride,
@@ -1638,8 +1727,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   if (!uniform_task<BS>(context_lens, num_seqs, kv_heads, max_ctx, t, gridDim.x, &tk)) return;
   const int32_t s = tk.s, g = tk.g;
   const int q_heads = kv_heads * G;
-  if (kv_slots && tk.p == tk.n - 1)   // the unit's last partition owns the new token
-    append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
+  const bool owner = APPEND && tk.p == tk.n - 1;   // the unit's last partition owns the new token
   if (tk.p == 0 && threadIdx.x == 0) {
     const int64_t u = static_cast<int64_t>(s) * kv_heads + g;
     unit_desc[2 * u] = tk.t0;
@@ -1648,6 +1736,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   const int32_t len = context_lens[s];
   const bool bad_len = len < 0 || len > max_ctx;
   if (bad_len || len == 0) {
+    if (owner) append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
     fill_rows<D, G>(out, out_dtype, s, q_heads, g, g + 1, bad_len ? qnan() : 0.f);
     return;
   }
@@ -1657,8 +1746,10 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
   const int32_t* table = block_tables + static_cast<int64_t>(s) * table_stride;
   __shared__ WaveMerge<NW, G, D, kUseMfma<DT, BS, G>> sh;
   const bool shared = shares_first_block(block_tables, table_stride, s, num_seqs);
-  attend_range_policy<DT, D, BS, G, NW>(
-      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, sh,
+  const NewToken nt =
+      owner ? new_token_of<DT, D, BS>(k_new, v_new, kv_slots, s, g, kv_heads, num_blocks, len) : NewToken{};
+  attend_range_policy<DT, D, BS, G, NW, APPEND>(
+      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         if (single) {
           const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
@@ -1672,6 +1763,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, false>)) void d
           part_ml[2 * rec + 1] = L;
         }
       });
+  if (owner) append_token<DT, D, BS>(k_pool, v_pool, k_new, v_new, kv_slots, s, g, kv_heads, num_blocks);
 }
 
 // ---------------------------------------------------------------------------
@@ -1748,11 +1840,13 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
     return hipGetLastError();
   }
   if (a.uniform) {
-    hipLaunchKernelGGL((decode_uniform_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
-                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), static_cast<const char*>(a.q),
-                       a.out, a.out_dtype, a.part_ml, a.part_o, a.unit_desc, a.block_tables, a.table_stride,
-                       a.context_lens, a.num_seqs, p.num_blocks, p.kv_heads, a.max_context_len, a.scale_log2,
-                       static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.kv_slots);
+    auto kernel = a.kv_slots ? decode_uniform_kernel<DT, D, BS, G, kWaves, true>
+                             : decode_uniform_kernel<DT, D, BS, G, kWaves, false>;
+    hipLaunchKernelGGL(kernel, dim3(a.grid), dim3(kThreads), 0, stream, static_cast<const char*>(p.k),
+                       static_cast<const char*>(p.v), static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml,
+                       a.part_o, a.unit_desc, a.block_tables, a.table_stride, a.context_lens, a.num_seqs,
+                       p.num_blocks, p.kv_heads, a.max_context_len, a.scale_log2, static_cast<const char*>(a.k_new),
+                       static_cast<const char*>(a.v_new), a.kv_slots);
     hipError_t e = hipGetLastError();
     // with no more than one workgroup per unit and kv-head nothing splits (uniform_task)
     if (e != hipSuccess || a.grid / p.kv_heads <= a.num_seqs) return e;
@@ -1790,8 +1884,9 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   // extra column's workgroups return at once, like any partition past a
   // context's end.
   dim3 grid(suffix_parts | 1, p.kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, BS, G, kWaves>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const char*>(p.k), static_cast<const char*>(p.v),
+  auto kernel = a.kv_slots ? decode_partition_kernel<DT, D, BS, G, kWaves, true>
+                           : decode_partition_kernel<DT, D, BS, G, kWaves, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const char*>(p.k), static_cast<const char*>(p.v),
                      static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
                      a.table_stride, a.context_lens, seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads,
                      a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2,
@@ -1846,9 +1941,9 @@ struct CapacityFn {
     static int partition_cache[64], uniform_cache[64];
     hipError_t e = balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, &cap->balanced_grid);
     if (e != hipSuccess) return e;
-    e = resident_workgroups(decode_partition_kernel<DT, D, BS, G, kWaves>, partition_cache, &cap->partition);
+    e = resident_workgroups(decode_partition_kernel<DT, D, BS, G, kWaves, false>, partition_cache, &cap->partition);
     if (e != hipSuccess) return e;
-    return resident_workgroups(decode_uniform_kernel<DT, D, BS, G, kWaves>, uniform_cache, &cap->uniform);
+    return resident_workgroups(decode_uniform_kernel<DT, D, BS, G, kWaves, false>, uniform_cache, &cap->uniform);
   }
 };
 
