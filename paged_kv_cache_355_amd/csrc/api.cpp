@@ -87,7 +87,8 @@ struct DecodePlan {
   bool balanced = false;
   bool uniform = false;          // uniform split: `grid` workgroups, unit descriptors at desc_off
   int64_t desc_off = 0;
-  int32_t partition_tokens = 0;  // fixed partitions
+  int32_t partition_tokens = 0;  // fixed partitions: tokens per workgroup
+  int32_t wave_tokens = 0;       // > 0: the caller's partition length, one partition per wave
   int32_t max_parts = 1;
   int32_t grid = 0;              // balanced split
   int32_t num_slots = 0;
@@ -138,6 +139,18 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
                                       std::to_string(d.block_size) + ")");
     plan->partition_tokens = p;
     plan->max_parts = static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, p)));
+    // Short partitions are taken one per wave, kDecodeWaves consecutive ones
+    // to a workgroup: each wave streams its partition as one run and the
+    // workgroup merges their (max, sum, output) in LDS before it writes one
+    // record, so the reduce kernel reads a quarter of the records.
+    const int32_t ct = pa::decode_chunk_tokens(d.dtype, d.head_dim, d.block_size, group);
+    if (plan->max_parts > 1 && p <= pa::kGroupedPartitionTokens && p % ct == 0 &&
+        int64_t{pa::kDecodeWaves} * p <= int64_t{pa::kTableBatch} * d.block_size) {
+      plan->wave_tokens = p;
+      plan->partition_tokens = pa::kDecodeWaves * p;
+      plan->max_parts =
+          static_cast<int32_t>(std::max<int64_t>(1, ceil_div(max_context_len, plan->partition_tokens)));
+    }
     if (plan->max_parts > 1) layout_records(plan, static_cast<int64_t>(num_seqs) * q_heads * plan->max_parts, d.head_dim);
     return PA_OK;
   }
@@ -423,7 +436,10 @@ pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int3
     return fail(PA_ERR_INVALID, "bad sizes");
   DecodePlan plan;
   if (pa_status s = plan_decode(pool, num_seqs, q_heads, max_context_len, partition_tokens, &plan)) return s;
-  *resolved = plan.balanced ? PA_PARTITION_BALANCED : plan.uniform ? PA_PARTITION_UNIFORM : plan.partition_tokens;
+  *resolved = plan.balanced  ? PA_PARTITION_BALANCED
+              : plan.uniform ? PA_PARTITION_UNIFORM
+              : plan.wave_tokens > 0 ? plan.wave_tokens
+                                     : plan.partition_tokens;
   return PA_OK;
 }
 
@@ -508,6 +524,7 @@ pa_status decode_call(const pa_pool* pool, void* out, pa_dtype out_dtype, const 
   a.grid = plan.grid;
   a.num_slots = plan.num_slots;
   a.partition_tokens = plan.partition_tokens;
+  a.wave_tokens = plan.wave_tokens;
   a.max_parts = plan.max_parts;
   if (plan.bytes > 0) {
     char* ws = static_cast<char*>(workspace);

@@ -62,7 +62,7 @@ namespace pa {
 namespace dec {
 
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so 2^(m - m') never sees inf - inf
-constexpr int kWaves = 4;
+constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = kWaves * 64;
 constexpr int kFanIn = 16;      // records merged per node of the balanced kernel's merge tree
 constexpr int kMaxLevels = 3;   // kFanIn^3 = 4096 ≥ pieces of any unit (≤ grid + 1)
@@ -204,8 +204,8 @@ struct Chunk {
 };
 
 // LDS of one workgroup: the block ids of the range being read, staged once
-// per batch, and the buffers through which the NW waves merge their results.
-constexpr int kTableBatch = 512;   // block ids staged per batch (a multiple of every CT / BS)
+// per batch (kTableBatch of them, a multiple of every CT / BS), and the
+// buffers through which the NW waves merge their results.
 
 // The matrix-core path: 16-bit K/V, blocks of at least 16 tokens (one 16-token
 // MFMA tile never straddles a block) and at least 4 query rows per kv-head
@@ -287,6 +287,25 @@ __device__ __forceinline__ uint4 load_kv(const char* p) {
 //                    V transposed.  Loading K straight into the A layout
 //                    would split every 128-byte line over two instructions.
 // ---------------------------------------------------------------------------
+// The chunks of a table batch (tokens [tb, te), chunks of CT tokens from tb)
+// that this wave takes: [first, limit).  Each wave takes one contiguous run of
+// the workgroup's range [t_begin, t_end): wave w the tokens [t_begin +
+// w·wt, +wt), where wt is wave_tokens when given (> 0: one caller partition
+// per wave) or else the range split in NW runs, rounded up to whole chunks (so
+// the runs meet on chunk bounds).
+struct ChunkDeal {
+  int32_t first, limit;
+};
+template <int CT, int NW>
+__device__ __forceinline__ ChunkDeal deal_chunks(int32_t wave, int32_t wave_tokens, int32_t t_begin, int32_t t_end,
+                                                 int32_t tb, int32_t te) {
+  const int32_t wt = wave_tokens > 0 ? wave_tokens : ((t_end - t_begin + NW * CT - 1) / (NW * CT)) * CT;
+  const int32_t lo = max(t_begin + wave * wt, tb);
+  const int32_t hi = min(t_begin + (wave + 1) * wt, te);
+  if (lo >= hi) return {0, 0};
+  return {(lo - tb) / CT, (hi - tb + CT - 1) / CT};
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -377,8 +396,8 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
                                                   const char* q_lane, const char* __restrict__ q_dummy,
                                                   const int32_t* __restrict__ table, int32_t g, int32_t kv_heads,
                                                   int32_t num_blocks, int32_t t_begin, int32_t t_end,
-                                                  float scale_log2, NewToken nt, WaveMerge<NW, R, D, true>& sh,
-                                                  Emit&& emit) {
+                                                  float scale_log2, NewToken nt, int32_t wave_tokens,
+                                                  WaveMerge<NW, R, D, true>& sh, Emit&& emit) {
   constexpr int EB = 2;
   constexpr int ROW = D * EB;          // bytes per token row
   constexpr int CT = 16;               // tokens per chunk (the MFMA M dimension)
@@ -430,7 +449,6 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
     __syncthreads();
     const int32_t tb = max(t_begin, bb * BS);
     const int32_t te = min(t_end, (bb + nb) * BS);
-    const int32_t nchunks = (te - tb + CT - 1) / CT;
 
     // Issue chunk c's K and V loads (live = false: read q_dead, valid and
     // cache-resident).  Rows past te inside the block may be read; they are
@@ -548,16 +566,18 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
     };
 
     uint4 ka[NKL], va[NKL], kb2[NKL], vb2[NKL];
-    int32_t c = wave;
-    load_chunk(c, c < nchunks, ka, va);
-    for (; c < nchunks; c += 2 * NW) {
-      load_chunk(c + NW, c + NW < nchunks, kb2, vb2);
+    const ChunkDeal dl = deal_chunks<CT, NW>(wave, wave_tokens, t_begin, t_end, tb, te);
+    const int32_t lim = dl.limit;
+    int32_t c = dl.first;
+    load_chunk(c, c < lim, ka, va);
+    for (; c < lim; c += 2) {
+      load_chunk(c + 1, c + 1 < lim, kb2, vb2);
       __builtin_amdgcn_sched_barrier(0);
       consume_chunk(c, ka, va);
-      if (c + NW >= nchunks) break;
-      load_chunk(c + 2 * NW, c + 2 * NW < nchunks, ka, va);
+      if (c + 1 >= lim) break;
+      load_chunk(c + 2, c + 2 < lim, ka, va);
       __builtin_amdgcn_sched_barrier(0);
-      consume_chunk(c + NW, kb2, vb2);
+      consume_chunk(c + 1, kb2, vb2);
     }
   }
 
@@ -627,15 +647,15 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
                                              const char* __restrict__ q, const int32_t* __restrict__ table,
                                              int32_t s, int32_t g, int32_t kv_heads, int32_t num_blocks,
                                              int32_t t_begin, int32_t t_end, float scale_log2, NewToken nt,
-                                             WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
+                                             int32_t wave_tokens, WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh,
+                                             Emit&& emit) {
   if constexpr (kUseMfma<DT, BS, G>) {
     constexpr int EB = 2;
     const int tl = threadIdx.x & 15;
     const char* q_head0 = q + ((static_cast<int64_t>(s) * kv_heads * G + g * G) * D) * EB;   // row g·G of sequence s
     attend_range_mfma<DT, D, BS, G, NW, STREAM, NEWTOK>(k_pool, v_pool, tl < G ? q_head0 + tl * D * EB : nullptr,
-                                                        q_head0,
-                                                table, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, sh,
-                                                emit);
+                                                        q_head0, table, g, kv_heads, num_blocks, t_begin, t_end,
+                                                        scale_log2, nt, wave_tokens, sh, emit);
     return;
   } else {
   using S = Shape<DT, D>;
@@ -685,7 +705,6 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
     __syncthreads();
     const int32_t tb = max(t_begin, bb * BS);
     const int32_t te = min(t_end, (bb + nb) * BS);
-    const int32_t nchunks = (te - tb + CT - 1) / CT;
 
     // Byte offset of token t's row in its (block, kv-head) tile; t lies in this batch.
     auto tile_of = [&](int32_t t) {
@@ -799,16 +818,18 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
     // chunk's arithmetic above the next chunk's load issue, which would make
     // the wave wait for its data before the prefetch leaves.)
     uint4 ka[NLC], va[NLC], kb2[NLC], vb2[NLC];
-    int32_t c = wave;
-    load_chunk(c, c < nchunks, ka, va);
-    for (; c < nchunks; c += 2 * NW) {
-      load_chunk(c + NW, c + NW < nchunks, kb2, vb2);
+    const ChunkDeal dl = deal_chunks<CT, NW>(wave, wave_tokens, t_begin, t_end, tb, te);
+    const int32_t lim = dl.limit;
+    int32_t c = dl.first;
+    load_chunk(c, c < lim, ka, va);
+    for (; c < lim; c += 2) {
+      load_chunk(c + 1, c + 1 < lim, kb2, vb2);
       __builtin_amdgcn_sched_barrier(0);
       consume_chunk(c, ka, va);
-      if (c + NW >= nchunks) break;
-      load_chunk(c + 2 * NW, c + 2 * NW < nchunks, ka, va);
+      if (c + 1 >= lim) break;
+      load_chunk(c + 2, c + 2 < lim, ka, va);
       __builtin_amdgcn_sched_barrier(0);
-      consume_chunk(c + NW, kb2, vb2);
+      consume_chunk(c + 1, kb2, vb2);
     }
   }
 
@@ -967,14 +988,14 @@ __device__ __forceinline__ void attend_range_policy(bool shared, const char* __r
                                                     const char* __restrict__ v_pool, const char* __restrict__ q,
                                                     const int32_t* __restrict__ table, int32_t s, int32_t g,
                                                     int32_t kv_heads, int32_t num_blocks, int32_t t_begin,
-                                                    int32_t t_end, float scale_log2, NewToken nt,
+                                                    int32_t t_end, float scale_log2, NewToken nt, int32_t wave_tokens,
                                                     WaveMerge<NW, G, D, kUseMfma<DT, BS, G>>& sh, Emit&& emit) {
   if (shared) {
     attend_range<DT, D, BS, G, NW, false, NEWTOK>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin,
-                                                  t_end, scale_log2, nt, sh, emit);
+                                                  t_end, scale_log2, nt, wave_tokens, sh, emit);
   } else {
     attend_range<DT, D, BS, G, NW, true, NEWTOK>(k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin,
-                                                 t_end, scale_log2, nt, sh, emit);
+                                                 t_end, scale_log2, nt, wave_tokens, sh, emit);
   }
 }
 
@@ -996,7 +1017,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesExtra<DT, BS, G, APPEND>)) void 
     void* __restrict__ out, int32_t out_dtype, float* __restrict__ part_ml, float* __restrict__ part_o,
     const int32_t* __restrict__ block_tables, int32_t table_stride, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ seq_prefix, int32_t max_prefix, int32_t num_seqs, int32_t num_blocks,
-    int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, float scale_log2,
+    int32_t kv_heads, int32_t max_ctx, int32_t max_parts, int32_t part_tokens, int32_t wave_tokens, float scale_log2,
     const char* __restrict__ k_new, const char* __restrict__ v_new, const int32_t* __restrict__ kv_slots) {
   const int p = blockIdx.x;
   const int g = blockIdx.y;
@@ -1043,7 +1064,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesExtra<DT, BS, G, APPEND>)) void 
   const NewToken nt =
       owner ? new_token_of<DT, D, BS>(k_new, v_new, kv_slots, s, g, kv_heads, num_blocks, len_c) : NewToken{};
   attend_range_policy<DT, D, BS, G, NW, APPEND>(
-      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, sh,
+      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, wave_tokens, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
         if (nsp == 1) {
@@ -1122,10 +1143,10 @@ __global__ __launch_bounds__(NW * 64, 3) void decode_prefix_kernel(
   };
   if (m_end - m_begin <= MT) {
     attend_range_mfma<DT, D, BS, 16, NW, true, false>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
-                                               t_begin, t_end, scale_log2, NewToken{}, sh, emit);
+                                               t_begin, t_end, scale_log2, NewToken{}, 0, sh, emit);
   } else {
     attend_range_mfma<DT, D, BS, 16, NW, false, false>(k_pool, v_pool, q_lane, q_dummy, table, g, kv_heads, num_blocks,
-                                                t_begin, t_end, scale_log2, NewToken{}, sh, emit);
+                                                t_begin, t_end, scale_log2, NewToken{}, 0, sh, emit);
   }
 }
 
@@ -1543,7 +1564,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesPerEU<DT, BS, G, true>)) void de
       int32_t idx = static_cast<int32_t>(w - first_w);
       const int64_t my_slot = slot0 + idx;
       attend_range_policy<DT, D, BS, G, NW, false>(
-          shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, NewToken{}, sh,
+          shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t0, t1, scale_log2, NewToken{}, 0, sh,
           [&](int r, int d, float M, float L, float O, bool bad) {
             if (whole) {
               const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
@@ -1749,7 +1770,7 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesExtra<DT, BS, G, true>)) void de
   const NewToken nt =
       owner ? new_token_of<DT, D, BS>(k_new, v_new, kv_slots, s, g, kv_heads, num_blocks, len) : NewToken{};
   attend_range_policy<DT, D, BS, G, NW, APPEND>(
-      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, sh,
+      shared, k_pool, v_pool, q, table, s, g, kv_heads, num_blocks, t_begin, t_end, scale_log2, nt, 0, sh,
       [&](int r, int d, float M, float L, float O, bool bad) {
         if (single) {
           const int64_t row = static_cast<int64_t>(s) * q_heads + g * G + r;
@@ -1831,6 +1852,8 @@ void launch_reduce(const DecodeArgs& a, const int32_t* seq_prefix, const int32_t
 
 template <int DT, int D, int BS, int G>
 hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stream) {
+  static_assert(decode_chunk_tokens(DT, D, BS, G) == (kUseMfma<DT, BS, G> ? 16 : Chunk<DT, D, BS>::CT),
+                "the host's chunk length differs from the kernels'");
   if (a.kv_slots && (a.balanced || a.group_start)) return hipErrorInvalidValue;   // the host writes first there
   if (a.balanced) {
     hipLaunchKernelGGL((decode_balanced_kernel<DT, D, BS, G, kWaves>), dim3(a.grid), dim3(kThreads), 0, stream,
@@ -1886,11 +1909,11 @@ hipError_t launch_typed(const PoolDesc& p, const DecodeArgs& a, hipStream_t stre
   dim3 grid(suffix_parts | 1, p.kv_heads, a.num_seqs);
   auto kernel = a.kv_slots ? decode_partition_kernel<DT, D, BS, G, kWaves, true>
                            : decode_partition_kernel<DT, D, BS, G, kWaves, false>;
-  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const char*>(p.k), static_cast<const char*>(p.v),
-                     static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml, a.part_o, a.block_tables,
-                     a.table_stride, a.context_lens, seq_prefix, a.max_prefix, a.num_seqs, p.num_blocks, p.kv_heads,
-                     a.max_context_len, a.max_parts, a.partition_tokens, a.scale_log2,
-                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.kv_slots);
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, static_cast<const char*>(p.k),
+                     static_cast<const char*>(p.v), static_cast<const char*>(a.q), a.out, a.out_dtype, a.part_ml,
+                     a.part_o, a.block_tables, a.table_stride, a.context_lens, seq_prefix, a.max_prefix, a.num_seqs,
+                     p.num_blocks, p.kv_heads, a.max_context_len, a.max_parts, a.partition_tokens, a.wave_tokens,
+                     a.scale_log2, static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.kv_slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || suffix_parts <= 1) return e;
   launch_reduce<D, BS, G>(a, seq_prefix, nullptr, stream);

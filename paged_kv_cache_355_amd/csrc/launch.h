@@ -9,7 +9,7 @@ namespace pa {
 
 enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-inline int32_t elem_bytes(int32_t dt) { return dt == kF32 ? 4 : 2; }
+constexpr int32_t elem_bytes(int32_t dt) { return dt == kF32 ? 4 : 2; }
 
 // Largest grid of the balanced decode kernel (its merge tree holds at most
 // 16^3 records per unit, and a unit meets at most grid + 1 workgroups).
@@ -25,6 +25,25 @@ constexpr int32_t kMergeLevels = 3;
 // workspace without writing over the counters.
 constexpr int32_t kCounterSlots = kMaxBalancedGrid + 1;
 constexpr int64_t kCounterBytes = int64_t{kMergeLevels} * kCounterSlots * 4;   // 48 KiB, a multiple of 256
+
+// Waves per decode workgroup, and block ids a workgroup stages at a time.
+constexpr int32_t kDecodeWaves = 4;
+constexpr int32_t kTableBatch = 512;
+// Fixed partitions of at most this many tokens are taken one per wave, four to
+// a workgroup (DecodeArgs::wave_tokens).
+constexpr int32_t kGroupedPartitionTokens = 512;
+
+// Tokens per chunk of the decode inner loops: the 16-token matrix-core tile
+// (16-bit K/V, blocks of ≥ 16 tokens, ≥ 4 query rows per kv-head), else four
+// (one for blocks shorter than a load) wave-wide 16-byte loads of
+// 64 / (head_dim · element bytes / 16) tokens each.  decode_impl.h checks that
+// its loops use the same.
+constexpr int32_t decode_chunk_tokens(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
+  return (dtype != kF32 && block_size >= 16 && group >= 4)
+             ? 16
+             : (block_size < 64 / (head_dim * elem_bytes(dtype) / 16) ? 1 : 4) *
+                   (64 / (head_dim * elem_bytes(dtype) / 16));
+}
 
 struct PoolDesc {
   int32_t num_blocks, block_size, kv_heads, head_dim, dtype;
@@ -58,6 +77,11 @@ struct DecodeArgs {
   // Fixed partitions (balanced = false, uniform = false).
   int32_t partition_tokens;
   int32_t max_parts;       // partitions covering max_context_len
+  // > 0: each partition of partition_tokens is kDecodeWaves consecutive runs
+  // of wave_tokens tokens, one per wave of its workgroup (the caller's
+  // partitions, merged in LDS before the record is written); 0: the
+  // partition's chunks are dealt to the waves in turn.
+  int32_t wave_tokens = 0;
   // Partial records.  Fixed partitions: [num_seqs][q_heads][max_parts] rows;
   // balanced: [num_slots][group] rows; uniform: [grid][group] rows.
   float* part_ml;          // rows × (max, sum)

@@ -320,15 +320,17 @@ def test_balanced_workspace_reuse_leaves_counters_zero(gpu):
         assert np.max(np.abs(out_to_f64(out) - want[:n])) <= TOL["f16"]
 
 
-def test_one_workspace_serves_every_split_mode(gpu):
+def test_one_workspace_serves_every_split_mode(gpu, monkeypatch):
     """One workspace, zero-filled once and sized to the largest split of the
     batch, serves fixed partitions, the balanced split and the uniform split
-    in any order.  The fixed-partition plan needs the most bytes here, so its
-    records reach furthest into the workspace; the balanced calls that follow
-    must still find their merge counters at zero (PA_DEBUG_VALIDATE checks them
-    before each call) and every output matches the oracle."""
+    in any order.  With a 16-workgroup balanced grid the 16-token partitions
+    need the most bytes, so their records reach past everything the balanced
+    plan lays out; the balanced calls that follow must still find their merge
+    counters at zero (PA_DEBUG_VALIDATE checks them before each call) and
+    every output matches the oracle."""
     import torch
     pk = gpu
+    monkeypatch.setenv("PA_DECODE_GRID", "16")
     case = build_case([2500, 17, 900, 1300, 64, 2047], 2, 4, 64, 16, "f16", 6, scale=1.0)
     want = paged_decode(case["q"], case["k_pool"], case["v_pool"], case["tables"], case["lens"], "f16")
     pool = pk.Pool(case["num_blocks"], 16, 2, 64, "f16", k=to_torch(case["k_pool"], "f16"),
@@ -338,7 +340,7 @@ def test_one_workspace_serves_every_split_mode(gpu):
     bal, uni = pk.PA_PARTITION_BALANCED, pk.PA_PARTITION_UNIFORM
     modes = [64, bal, uni, bal, 512, bal, uni, 16, bal]
     sizes = {m: pk.decode_workspace_bytes(pool, 6, 8, 2500, m) for m in set(modes)}
-    assert sizes[16] == max(sizes.values()) > sizes[bal]   # the longest records reach past the balanced plan
+    assert sizes[16] == max(sizes.values()) > sizes[bal]   # the fixed records reach past the balanced plan
     ws = torch.zeros(max(sizes.values()), dtype=torch.uint8, device="cuda")
     for m in modes:
         out = pk.decode(pool, q, tables, lens, 2500, out_dtype="f32", workspace=ws, partition_tokens=m)
