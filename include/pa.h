@@ -134,7 +134,9 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* s
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace pa_decode needs for these sizes (0 when no
- * partial results are kept).  partition_tokens as for pa_decode.  The
+ * partial results are kept): the partial (max, sum, output) records of the
+ * tiled softmax's pieces before they are merged ([P2] §4.1), after the
+ * balanced split's merge counters.  partition_tokens as for pa_decode.  The
  * automatic choice and the balanced split depend on the current device's CU
  * count and occupancy, so ask on the device that will decode.
  * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
@@ -147,9 +149,12 @@ pa_status pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32
 #define PA_PARTITION_BALANCED -1
 #define PA_PARTITION_UNIFORM -2
 
-/* How pa_decode will split these sizes: the partition length in tokens (a
+/* How pa_decode will split these sizes into the pieces of [P2] §4.1's tiled
+ * softmax, whose lengths differ per sequence ([P2] §4.3: a batch's sequences
+ * need different numbers of blocks): the partition length in tokens (a
  * length ≥ max_context_len means one workgroup per (sequence, kv-head)),
- * PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM. */
+ * PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM.
+ * Errors: PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP. */
 pa_status pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t q_heads,
                                      int32_t max_context_len, int32_t partition_tokens,
                                      int32_t* resolved);
@@ -450,12 +455,28 @@ pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap
  * PA_ERR_INVALID (cap too small; *n_blocks is set, nothing changes). */
 pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq_id, int32_t* blocks, int32_t cap, int32_t* n_blocks);
 
+/* The reference count of a physical block: the number of block tables that
+ * map one of their entries to it ([P2] §3.4: shared blocks are counted, and
+ * a block with a count above 1 is read-only; [P1] "跨请求的内存共享").
+ * 0 for a free block.  Errors: PA_ERR_INVALID (NULL pointer, block outside
+ * the pool). */
 pa_status pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t* rc);
 
 /* Free-list contents from head to tail (up to cap entries); *n receives the
- * number of free blocks. */
+ * number of free blocks ([P2] §3.3: the manager keeps a list of free
+ * physical blocks, finished requests return theirs to it, and any free block
+ * may serve any request; the head is handed out next).  out may be NULL to
+ * ask for the count.  Errors: PA_ERR_INVALID (cap smaller than the list;
+ * *n is set). */
 pa_status pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap, int32_t* n);
 
+/* The manager's occupancy counters (pa_bm_stats_t above), from which the
+ * pages' utilisation measures follow: slots holding a token over slots of the
+ * blocks in use — waste only in each sequence's last, part-filled block
+ * ([P1] "内存浪费的两种形式" and "Paged Attention 的工作原理": 2/4 of the
+ * last block against 6/16 of a contiguous reservation; [P2] §3.3: above 99 %
+ * utilisation) — and logical over physical blocks, the saving of blocks
+ * shared by refcount ([P2] §3.4).  Errors: PA_ERR_INVALID (NULL pointer). */
 pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
 
 #ifdef __cplusplus

@@ -1370,6 +1370,20 @@ __device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t C, int64_t W) 
 // issues its loads only after the increment that tells it it is last.  (A
 // workgroup-scope fence or barrier does not wait for global stores on this
 // target, so the wait is explicit.)
+//
+// This ordering rests on gfx950 hardware behaviour, not on the C++/HIP memory
+// model, which would ask for a release increment and an acquire read of the
+// counter (each compiles to a device-wide cache write-back or invalidate here,
+// and a fence per cut piece made the kernel 2.8x slower).  The assumptions:
+//  * a store with device scope (sc1) is counted complete by vmcnt only once
+//    it has reached the level that every XCD reads through, so after
+//    wait_vmem no XCD can observe the record's old value;
+//  * a load with device scope is served from that level, never from a stale
+//    line in the reader's own L2, and a load issued after the counter's
+//    atomic has returned (the reader branches on the returned value) cannot
+//    be satisfied before the atomic.
+// The balanced split is opt-in (PA_PARTITION_BALANCED) and is checked against
+// the oracle on grids of 1 to 4000 workgroups (three-level merge trees).
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited on
 }
