@@ -228,16 +228,21 @@ constexpr int kMinWavesExtra = (EXTRA && !kUseMfma<DT, BS, G> && G == 2) ? 3 : k
 
 template <int NW, int G, int D, bool MFMA>
 struct WaveMerge {
-  // matrix-core path: each wave's V tile, 16 tokens × D.  Lane quarter qd
-  // reads rows 4qd..4qd+3; a row of D/2 + 2 dwords puts the quarters 8 banks
-  // apart (4·(D/2 + 2) ≡ 8 mod 32), so one transposed read touches 32
-  // distinct banks.  kt is the K tile, read back in the A layout.
+  // matrix-core path: each wave's K and V tiles, 16 tokens × D, rows
+  // 16-byte aligned so each lane stores its 16-byte piece of a token row with
+  // one write.  The row lengths were chosen by counting SQ_LDS_BANK_CONFLICT
+  // on gfx950 (70B-layer GQA batch, per decode call): kt of D + 16 and vt of
+  // D + 8 elements leave no conflicts in the row writes, the A-layout
+  // read-back of K or the transposed read of V.  Rows of D + 4 elements
+  // (8-byte aligned, two 8-byte writes per piece) cost 5.4 M conflict cycles
+  // in each tile's writes; kt of D + 8, D + 24 … D + 40 cost 2.7 M in its
+  // read-back, D + 64 8.1 M.
   struct Tiles {
-    uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
-    uint16_t kt[MFMA ? NW : 1][16][MFMA ? D + 4 : 1];
+    alignas(16) uint16_t vt[MFMA ? NW : 1][16][MFMA ? D + 8 : 1];
+    alignas(16) uint16_t kt[MFMA ? NW : 1][16][MFMA ? D + 16 : 1];
   };
   union {             // the tiles live during the token loop, o after it
-    float o[NW][G][D];
+    float o[NW][G][D];  // matrix-core path: 4-float groups XOR-swizzled by row (wave_out)
     Tiles t;
   };
   float m[NW][G];
@@ -287,6 +292,13 @@ __device__ __forceinline__ uint4 load_kv(const char* p) {
 //                    V transposed.  Loading K straight into the A layout
 //                    would split every 128-byte line over two instructions.
 // ---------------------------------------------------------------------------
+// Column of output element (row, col) in a wave's merge buffer of the
+// matrix-core path: its 4-float groups are XOR-swizzled by row, so the
+// lanes of one row group (4 consecutive floats each, rows 8 apart in banks
+// otherwise) write distinct banks; readers take consecutive columns of one
+// row, which the swizzle keeps distinct too.
+__device__ __forceinline__ int wave_out(int row, int col) { return col ^ (4 * (row & 7)); }
+
 // The chunks of a table batch (tokens [tb, te), chunks of CT tokens from tb)
 // that this wave takes: [first, limit).  Each wave takes one contiguous run of
 // the workgroup's range [t_begin, t_end): wave w the tokens [t_begin +
@@ -486,18 +498,14 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
         const int row = i * RPI + vrow;
-        uint2* dst = reinterpret_cast<uint2*>(&sh.t.kt[wave][row][(lane % LPR) * 8]);
-        dst[0] = make_uint2(kb[i].x, kb[i].y);
-        dst[1] = make_uint2(kb[i].z, kb[i].w);
+        *reinterpret_cast<uint4*>(&sh.t.kt[wave][row][(lane % LPR) * 8]) = kb[i];
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       uint4 ka_op[NKL];
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
-        const uint2* src = reinterpret_cast<const uint2*>(&sh.t.kt[wave][tl][32 * i + 8 * qd]);
-        const uint2 lo = src[0], hi = src[1];
-        ka_op[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        ka_op[i] = *reinterpret_cast<const uint4*>(&sh.t.kt[wave][tl][32 * i + 8 * qd]);
       }
       // S = K·Qᵀ
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -509,9 +517,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       for (int i = 0; i < NKL; ++i) {
         const int row = i * RPI + vrow;
         const uint4 v = tok0 + row < te ? vb[i] : make_uint4(0u, 0u, 0u, 0u);
-        uint2* dst = reinterpret_cast<uint2*>(&sh.t.vt[wave][row][(lane % LPR) * 8]);   // rows are 8-byte aligned
-        dst[0] = make_uint2(v.x, v.y);
-        dst[1] = make_uint2(v.z, v.w);
+        *reinterpret_cast<uint4*>(&sh.t.vt[wave][row][(lane % LPR) * 8]) = v;
       }
       // online softmax of row tl over tokens 4qd..4qd+3
       float sc[4];
@@ -590,10 +596,9 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
   __syncthreads();
   if (tl < R) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sh.o[wave][tl][16 * b + 4 * qd + r] = ob[b][r];
-    }
+    for (int b = 0; b < NB; ++b)
+      *reinterpret_cast<float4*>(&sh.o[wave][tl][wave_out(tl, 16 * b + 4 * qd)]) =
+          make_float4(ob[b][0], ob[b][1], ob[b][2], ob[b][3]);
     if (qd == 0) {
       sh.m[wave][tl] = m;
       sh.l[wave][tl] = l;
@@ -616,7 +621,7 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
     for (int w = 0; w < NW; ++w) {
       const float a = exp2f_fast(sh.m[w][r] - mm);
       L += sh.l[w][r] * a;
-      O += sh.o[w][r][d] * a;
+      O += sh.o[w][r][wave_out(r, d)] * a;
     }
     emit(r, d, mm, L, O, bad);
   }
@@ -1382,8 +1387,8 @@ __device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t C, int64_t W) 
 //    line in the reader's own L2, and a load issued after the counter's
 //    atomic has returned (the reader branches on the returned value) cannot
 //    be satisfied before the atomic.
-// The balanced split is opt-in (PA_PARTITION_BALANCED) and is checked against
-// the oracle on grids of 1 to 4000 workgroups (three-level merge trees).
+// The balanced split is opt-in (PA_PARTITION_BALANCED); its results are tested
+// on grids of 1 to 4000 workgroups (three-level merge trees).
 __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited on
 }
