@@ -154,17 +154,22 @@ def split_meta(flat, B, stride):
 def prepare_run(pk, w, st, partition_arg=0, decode_arg="auto"):
     """What the timed steps need besides the state: the split (the workload's
     own unless partition_arg is not 0), whether the sharing-aware decode runs
-    (decode_arg "auto": when the batch has prefix groups), the device metadata
-    array with its views, a zero-filled decode workspace sized for the longest
-    context the steps reach, and the two pinned host buffers."""
+    (decode_arg "auto": when the batch has prefix groups), two device metadata
+    arrays with their views (step i uses array i mod 2, uploaded on a copy
+    stream while the previous step's kernels run), a zero-filled decode
+    workspace sized for the longest context the steps reach, and the two
+    pinned host buffers."""
     import torch
 
     B = st["B"]
     part = w.partition_tokens if partition_arg == 0 else partition_arg
     max_ctx_bound = st["stride"] * w.block_size
-    dev = {"flat": torch.empty(meta_len(B, st["stride"]), dtype=torch.int32, device="cuda")}
-    (dev["slots"], dev["lens"], dev["pairs"], dev["tables"], dev["group_start"],
-     dev["prefix"]) = split_meta(dev["flat"], B, st["stride"])
+    dev = {"meta": [], "copy_stream": torch.cuda.Stream()}
+    for _ in range(2):
+        m = {"flat": torch.empty(meta_len(B, st["stride"]), dtype=torch.int32, device="cuda"), "free": None}
+        (m["slots"], m["lens"], m["pairs"], m["tables"], m["group_start"],
+         m["prefix"]) = split_meta(m["flat"], B, st["stride"])
+        dev["meta"].append(m)
     # the sharing-aware decode when the batch has prefix groups (and it was not turned off)
     _, probe_prefix, _ = st["bm"].prefix_groups(st["ids"][st["bm"].dispatch_order(st["ids"])])
     shared_prefix = decode_arg == "shared" or (decode_arg == "auto" and int(probe_prefix.max(initial=0)) > 0)
@@ -203,11 +208,13 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
     L = lib()
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
+    copy_stream = dev["copy_stream"]
     B, stride = st["B"], st["stride"]
     row_bytes = 2 * w.kv_heads * w.head_dim * pk.api.ELEM_BYTES[w.dtype]   # K + V per token
     kv_bytes = []
     for i in range(n_steps):
         hb = hbufs[(step0 + i) % len(hbufs)]
+        meta = dev["meta"][(step0 + i) % len(dev["meta"])]
         if hb.copied is not None:
             hb.copied.synchronize()
         # the scheduler arranges the batch for dispatch (long sequences first,
@@ -222,19 +229,25 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
             n_groups, max_group = st["bm"].prefix_groups_into(st["ids"].ctypes.data, B, hb.group_start.data_ptr(),
                                                               hb.prefix.data_ptr())
             max_prefix = int(hb.prefix_np.max())
-        dev["flat"].copy_(hb.flat, non_blocking=True)
+        # the upload overlaps the previous step's kernels: it waits only for
+        # the step that last read this device array, and the decodes wait for it
         if hb.copied is None:
             hb.copied = torch.cuda.Event()
-        hb.copied.record(stream)
+        with torch.cuda.stream(copy_stream):
+            if meta["free"] is not None:
+                copy_stream.wait_event(meta["free"])
+            meta["flat"].copy_(hb.flat, non_blocking=True)
+            hb.copied.record(copy_stream)
+        stream.wait_event(hb.copied)
         ws = dev["workspace"]
         ws_bytes = ws.numel()
         for layer, pool in enumerate(st["pools"]):
             if n_cow:
-                check(L.pa_copy_blocks(pool.handle, dev["pairs"].data_ptr(), n_cow, sptr), "pa_copy_blocks")
+                check(L.pa_copy_blocks(pool.handle, meta["pairs"].data_ptr(), n_cow, sptr), "pa_copy_blocks")
             fused = fused_append and not shared_prefix
             if not fused:
                 check(L.pa_write_kv(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
-                                    dev["slots"].data_ptr(), B, sptr), "pa_write_kv")
+                                    meta["slots"].data_ptr(), B, sptr), "pa_write_kv")
             timed = timing is not None and (timing["all_layers"] or layer == (step0 + i) % len(st["pools"]))
             if timed:
                 ev0, ev1 = timing["free"].pop()
@@ -242,23 +255,26 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
             if shared_prefix:
                 check(L.pa_decode_shared_prefix(
                     pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype], st["q"][layer].data_ptr(),
-                    B, w.q_heads, dev["tables"].data_ptr(), stride, dev["lens"].data_ptr(), max_len, 0.0, n_groups,
-                    dev["group_start"].data_ptr(), dev["prefix"].data_ptr(), max_group, max_prefix, partition_tokens,
+                    B, w.q_heads, meta["tables"].data_ptr(), stride, meta["lens"].data_ptr(), max_len, 0.0, n_groups,
+                    meta["group_start"].data_ptr(), meta["prefix"].data_ptr(), max_group, max_prefix, partition_tokens,
                     ws.data_ptr(), ws_bytes, sptr), "pa_decode_shared_prefix")
             elif fused:   # the new token's KV write runs inside the decode launch
                 check(L.pa_decode_append(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
-                                         dev["slots"].data_ptr(), st["out"][layer].data_ptr(),
+                                         meta["slots"].data_ptr(), st["out"][layer].data_ptr(),
                                          pk.api.DTYPE_CODES[w.dtype], st["q"][layer].data_ptr(), B, w.q_heads,
-                                         dev["tables"].data_ptr(), stride, dev["lens"].data_ptr(), max_len, 0.0,
+                                         meta["tables"].data_ptr(), stride, meta["lens"].data_ptr(), max_len, 0.0,
                                          partition_tokens, ws.data_ptr(), ws_bytes, sptr), "pa_decode_append")
             else:
                 check(L.pa_decode(pool.handle, st["out"][layer].data_ptr(), pk.api.DTYPE_CODES[w.dtype],
-                                  st["q"][layer].data_ptr(), B, w.q_heads, dev["tables"].data_ptr(), stride,
-                                  dev["lens"].data_ptr(), max_len, 0.0, partition_tokens, ws.data_ptr(), ws_bytes,
+                                  st["q"][layer].data_ptr(), B, w.q_heads, meta["tables"].data_ptr(), stride,
+                                  meta["lens"].data_ptr(), max_len, 0.0, partition_tokens, ws.data_ptr(), ws_bytes,
                                   sptr), "pa_decode")
             if timed:
                 ev1.record(stream)
                 timing["used"].append((ev0, ev1))
+        if meta["free"] is None:
+            meta["free"] = torch.cuda.Event()
+        meta["free"].record(stream)   # this step's kernels are the last readers of meta
         # logical bytes (every sequence's tokens) and unique bytes (each filled slot once:
         # blocks shared by refcount are counted once)
         unique_slots = st["bm"].stats()["filled_slots"]

@@ -631,8 +631,8 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
 // ---------------------------------------------------------------------------
 // attend_range: the G query rows of kv-head g of sequence s over tokens
 // [t_begin, t_end), t_begin < t_end, t_begin a multiple of CT or (fixed
-// partitions) of block_size.  Chunks of CT tokens are dealt to the NW waves
-// round-robin.  Every thread then calls emit(r, d, M, L, O, bad) for its share
+// partitions) of block_size.  Each of the NW waves takes one contiguous run of
+// CT-token chunks (deal_chunks).  Every thread then calls emit(r, d, M, L, O, bad) for its share
 // of the G×D outputs: M is the running max (base 2), L = Σ 2^(score−M),
 // O = Σ 2^(score−M)·v[d] for query row r, and bad reports a block id outside
 // the pool (then the values are meaningless).  Ends with a barrier, so the

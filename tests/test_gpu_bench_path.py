@@ -3,16 +3,18 @@
 bench.py times decode steps that the parity tests elsewhere do not take in
 the same way: the batch is re-arranged by the dispatch order every step, the
 block manager writes the step's metadata straight into a ring of two pinned
-host buffers laid out as one int32 array, one asynchronous copy uploads it,
-and the decode calls read their tables, lengths, slots and groups through
-views of that one device array, with host validation off (no host copies or
+host buffers laid out as one int32 array, one asynchronous copy on a second
+stream uploads it into one of two device arrays while the previous step's
+kernels run, and the decode calls read their tables, lengths, slots and
+groups through views of that array, with host validation off (no host copies or
 synchronisation inside the calls).  These tests run that code (the bench's
 own build_state, prepare_run and run_steps) for a few steps and check, after
 every step, against the oracle's block manager run in lockstep:
 
 * the order the batch was arranged in, and the pinned metadata: slots,
   copy-on-write pairs, padded tables, lengths, prefix groups;
-* that the device copy of the metadata equals the pinned bytes;
+* that the device copy of the metadata (one of two arrays, uploaded on a
+  copy stream that overlaps the previous step) equals the pinned bytes;
 * the K and V pools of every layer, bit for bit (blocks the step sequence
   touches against the oracle's writes and copies; every other block
   unchanged);
@@ -81,8 +83,10 @@ CASES = [
     ("mha7b_fp16", None, "auto", False),
     ("mha7b_fp16", None, "auto", True),
     ("gqa70b_bf16", 64, "auto", False),
+    ("gqa70b_bf16", 64, "auto", True),
     ("prefix_share_fp16", 64, "auto", False),     # prefix groups: pa_decode_shared_prefix
     ("long_splitk_bf16", None, "auto", False),    # 512-token partitions + reduce
+    ("long_splitk_bf16", None, "auto", True),
 ]
 
 
@@ -131,7 +135,8 @@ def test_timed_steps_match_the_oracle(gpu, name, batch, decode, fused):
             starts, prefix, _ = ora.prefix_groups(ids)
             assert hb.group_start.numpy()[:len(starts)].tolist() == starts, f"step {i}: group starts"
             assert hb.prefix.numpy().tolist() == prefix, f"step {i}: prefix tokens"
-        assert torch.equal(run["dev"]["flat"].cpu(), hb.flat), f"step {i}: uploaded metadata differs"
+        meta = run["dev"]["meta"][i % len(run["dev"]["meta"])]
+        assert torch.equal(meta["flat"].cpu(), hb.flat), f"step {i}: uploaded metadata differs"
         checked = range(layers) if i == n_steps - 1 else [i % layers]
         outs = {layer: out_to_f64(st["out"][layer]) for layer in checked}
         history.append(dict(slots=o_slots, pairs=o_pairs, tables=np.array(o_tables, dtype=np.int32),
