@@ -196,8 +196,13 @@ pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void
  *   partition_tokens: how the context is split into work ([P2] §4.1's tiled
  *     softmax, merged with running max and sum):
  *       > 0 — fixed partitions of that many tokens (a multiple of
- *           block_size), one workgroup each, merged by a second reduce
- *           kernel when a sequence has more than one;
+ *           block_size), merged by a second reduce kernel when a sequence
+ *           has more than one.  Partitions of at most 512 tokens that hold
+ *           whole chunks of the inner loop (16 tokens for 16-bit K/V with a
+ *           group of ≥ 4 and blocks of ≥ 16 tokens; 8 to 32 on the vector
+ *           loop) are taken one per wave, four consecutive ones to a
+ *           workgroup, which merges them before it writes one partial result;
+ *           longer ones take one workgroup each;
  *       PA_PARTITION_UNIFORM — one grid of workgroups, all resident at
  *           once; the device picks the shortest partition length (a
  *           multiple of block_size) whose partitions of every (sequence,

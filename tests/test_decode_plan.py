@@ -1,0 +1,177 @@
+"""Host-side decode planning through the C ABI, without a GPU.
+
+With a positive partition length the planning calls (pa_decode_partition_tokens,
+pa_decode_workspace_bytes, pa_decode_shared_prefix_workspace_bytes) need no
+device: the split is fixed by the sizes.  A pool over caller memory is only
+described, never touched, so host buffers stand in for the arrays.  The
+expected values restate the contract that include/pa.h documents:
+
+* the workspace is empty when no sequence is split; otherwise its first 48 KiB
+  hold the balanced split's merge counters and the records follow: (max, sum)
+  per row and partition, padded to 256 bytes, then the fp32 partial outputs;
+* partitions of at most 512 tokens that hold whole chunks of the kernel's
+  inner loop are taken one per wave, four consecutive ones to a workgroup,
+  which writes one record for the four; the partition length reported is
+  still the caller's;
+* the shared-prefix decode keeps records for the prefix's partitions and the
+  context's.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_355_amd._lib import lib
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED = 0, -1, -2
+DTYPES = {"f32": (0, 4), "f16": (1, 2), "bf16": (2, 2)}
+COUNTER_BYTES = 48 * 1024
+WAVES = 4
+GROUPED_MAX = 512
+TABLE_BATCH = 512
+
+
+class HostPool:
+    """A pool descriptor over 256-byte aligned host buffers (never dereferenced)."""
+
+    def __init__(self, num_blocks, block_size, kv_heads, head_dim, dtype):
+        code, elem = DTYPES[dtype]
+        nbytes = num_blocks * kv_heads * block_size * head_dim * elem
+        self._bufs = [np.zeros(nbytes + 256, dtype=np.uint8) for _ in range(2)]
+        ptrs = [b.ctypes.data + (-b.ctypes.data) % 256 for b in self._bufs]
+        self.handle = ctypes.c_void_p()
+        rc = lib().pa_alloc_pool(num_blocks, block_size, kv_heads, head_dim, code, ptrs[0], ptrs[1],
+                                 ctypes.byref(self.handle))
+        assert rc == PA_OK
+        self.block_size, self.kv_heads, self.head_dim, self.dtype = block_size, kv_heads, head_dim, dtype
+
+    def __del__(self):
+        lib().pa_free_pool(self.handle)
+
+
+def chunk_tokens(dtype, head_dim, block_size, group):
+    """Tokens the decode loop reads per chunk: 16 on the matrix-core path
+    (16-bit K/V, blocks of ≥ 16 tokens, ≥ 4 query rows per kv-head); on the
+    vector path four wave-wide 16-byte loads per tensor (one if a block holds
+    fewer tokens than one load covers)."""
+    elem = DTYPES[dtype][1]
+    if dtype != "f32" and block_size >= 16 and group >= 4:
+        return 16
+    tokens_per_load = 64 // (head_dim * elem // 16)
+    return (1 if block_size < tokens_per_load else 4) * tokens_per_load
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+def record_bytes(rows, head_dim):
+    return COUNTER_BYTES + ceil_div(rows * 2 * 4, 256) * 256 + rows * head_dim * 4
+
+
+def expected_plan(pool, num_seqs, q_heads, max_ctx, p):
+    """(reported partition length, workspace bytes) for a fixed partition length p."""
+    group = q_heads // pool.kv_heads
+    per_wg, parts = p, max(1, ceil_div(max_ctx, p))
+    if (parts > 1 and p <= GROUPED_MAX and p % chunk_tokens(pool.dtype, pool.head_dim, pool.block_size, group) == 0
+            and WAVES * p <= TABLE_BATCH * pool.block_size):
+        per_wg = WAVES * p
+        parts = max(1, ceil_div(max_ctx, per_wg))
+    if parts == 1:
+        return p, 0
+    return p, record_bytes(num_seqs * q_heads * parts, pool.head_dim)
+
+
+def plan(pool, num_seqs, q_heads, max_ctx, p):
+    L = lib()
+    resolved, nbytes = ctypes.c_int32(), ctypes.c_int64()
+    rc1 = L.pa_decode_partition_tokens(pool.handle, num_seqs, q_heads, max_ctx, p, ctypes.byref(resolved))
+    rc2 = L.pa_decode_workspace_bytes(pool.handle, num_seqs, q_heads, max_ctx, p, ctypes.byref(nbytes))
+    return rc1, rc2, resolved.value, nbytes.value
+
+
+CASES = [
+    # dtype, head_dim, block_size, kv_heads, group, num_seqs, max_ctx, partition
+    ("bf16", 128, 32, 1, 8, 8, 131072, 512),    # the long-context batch: grouped
+    ("bf16", 128, 32, 1, 8, 8, 131072, 544),    # above 512: one workgroup per partition
+    ("bf16", 128, 32, 1, 8, 8, 131072, 2048),
+    ("f16", 128, 16, 32, 1, 64, 2096, 2096),    # one partition: whole sequences, no workspace
+    ("f16", 128, 16, 32, 1, 64, 2096, 512),
+    ("f16", 128, 16, 32, 1, 64, 2096, 16),      # one block per partition: grouped
+    ("f16", 64, 4, 2, 2, 5, 1000, 4),           # chunk of 8 tokens on 4-token blocks: 4 is not whole chunks
+    ("f16", 64, 4, 2, 2, 5, 1000, 8),
+    ("f32", 128, 8, 3, 2, 17, 3001, 8),         # fp32 d128: 8-token chunks
+    ("f32", 64, 64, 1, 4, 3, 70000, 64),
+    ("bf16", 64, 64, 4, 4, 9, 5000, 320),       # 4 × 320 tokens ≤ 512 blocks of 64
+    ("f16", 128, 4, 1, 8, 2, 9000, 512),        # 4 × 512 tokens fill one batch of 512 staged 4-token blocks
+]
+
+
+@pytest.mark.parametrize("dtype,head_dim,block_size,kv_heads,group,num_seqs,max_ctx,p", CASES)
+def test_fixed_partition_plan_matches_the_documented_layout(dtype, head_dim, block_size, kv_heads, group, num_seqs,
+                                                            max_ctx, p):
+    pool = HostPool(64, block_size, kv_heads, head_dim, dtype)
+    q_heads = kv_heads * group
+    rc1, rc2, resolved, nbytes = plan(pool, num_seqs, q_heads, max_ctx, p)
+    assert (rc1, rc2) == (PA_OK, PA_OK)
+    want_resolved, want_bytes = expected_plan(pool, num_seqs, q_heads, max_ctx, p)
+    assert resolved == want_resolved
+    assert nbytes == want_bytes
+    if nbytes:
+        # the records never reach into the counter region, and hold (max, sum, output) per row and part
+        assert nbytes - COUNTER_BYTES >= num_seqs * q_heads * 2 * 4 + num_seqs * q_heads * head_dim * 4
+
+
+def test_grouping_quarters_the_long_context_records():
+    """The long-context batch at its 512-token partitions keeps one record per
+    2048 tokens: a quarter of the per-partition records."""
+    pool = HostPool(64, 32, 1, 128, "bf16")
+    _, _, _, grouped = plan(pool, 8, 8, 131072, 512)
+    _, _, _, per_partition = plan(pool, 8, 8, 131072, 544)   # one record per 544 tokens
+    rows = 8 * 8
+    assert grouped == record_bytes(rows * 64, 128)
+    assert per_partition == record_bytes(rows * ceil_div(131072, 544), 128)
+
+
+def test_empty_batch_needs_no_workspace():
+    pool = HostPool(64, 16, 2, 128, "f16")
+    rc1, rc2, resolved, nbytes = plan(pool, 0, 4, 1000, 64)
+    assert (rc1, rc2, nbytes) == (PA_OK, PA_OK, 0)
+
+
+@pytest.mark.parametrize("p,code", [(24, PA_ERR_INVALID), (-3, PA_ERR_INVALID), (-100, PA_ERR_INVALID)])
+def test_bad_partition_lengths_are_rejected(p, code):
+    pool = HostPool(64, 16, 2, 128, "f16")
+    rc1, rc2, _, _ = plan(pool, 4, 4, 1000, p)
+    assert rc1 == code and rc2 == code
+
+
+def test_unsupported_group_is_rejected():
+    pool = HostPool(64, 16, 2, 128, "f16")
+    rc1, rc2, _, _ = plan(pool, 4, 2 * 3, 1000, 64)    # group 3
+    assert rc1 == PA_ERR_UNSUPPORTED and rc2 == PA_ERR_UNSUPPORTED
+    rc1, rc2, _, _ = plan(pool, 4, 5, 1000, 64)        # q_heads not a multiple of kv_heads
+    assert rc1 == PA_ERR_INVALID and rc2 == PA_ERR_INVALID
+
+
+@pytest.mark.parametrize("max_prefix,p", [(1024, 1040), (1024, 512), (1008, 64), (16, 16)])
+def test_shared_prefix_workspace_holds_prefix_and_context_parts(max_prefix, p):
+    pool = HostPool(64, 16, 32, 128, "f16")
+    num_seqs, q_heads, max_ctx = 256, 32, 1040
+    nbytes = ctypes.c_int64()
+    rc = lib().pa_decode_shared_prefix_workspace_bytes(pool.handle, num_seqs, q_heads, max_ctx, max_prefix, p,
+                                                       ctypes.byref(nbytes))
+    assert rc == PA_OK
+    parts = ceil_div(max_prefix, p) + ceil_div(max_ctx, p)
+    assert nbytes.value == record_bytes(num_seqs * q_heads * parts, 128)
+
+
+def test_shared_prefix_without_a_prefix_sizes_like_pa_decode():
+    """No prefix (or pools the prefix kernel does not serve) means pa_decode's plan."""
+    for dtype, bs, max_prefix in [("f16", 16, 0), ("f32", 16, 512), ("f16", 8, 512)]:
+        pool = HostPool(64, bs, 2, 128, dtype)
+        nbytes = ctypes.c_int64()
+        rc = lib().pa_decode_shared_prefix_workspace_bytes(pool.handle, 8, 4, 2000, max_prefix, 64,
+                                                           ctypes.byref(nbytes))
+        assert rc == PA_OK
+        assert nbytes.value == plan(pool, 8, 4, 2000, 64)[3]
