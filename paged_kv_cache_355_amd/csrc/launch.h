@@ -79,8 +79,8 @@ struct DecodeArgs {
   int32_t max_parts;       // partitions covering max_context_len
   // > 0: each partition of partition_tokens is kDecodeWaves consecutive runs
   // of wave_tokens tokens, one per wave of its workgroup (the caller's
-  // partitions, merged in LDS before the record is written); 0: the
-  // partition's chunks are dealt to the waves in turn.
+  // partitions, merged in LDS before the record is written); 0: each wave
+  // takes one contiguous quarter of the partition's chunks.
   int32_t wave_tokens = 0;
   // Partial records.  Fixed partitions: [num_seqs][q_heads][max_parts] rows;
   // balanced: [num_slots][group] rows; uniform: [grid][group] rows.
