@@ -7,7 +7,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY names another build of the same C ABI (for instance a host
+# build under the sanitizers); by default the in-tree library.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 PA_OK = 0
 PA_ERR_INVALID = -1

@@ -774,7 +774,7 @@ static void write_rows(const pa::BlockManager& m, const int64_t* ids, int32_t n,
     if (tables) {
       int32_t* row = tables + static_cast<int64_t>(i) * stride;
       const int32_t nb = static_cast<int32_t>(t->size());
-      std::memcpy(row, t->data(), sizeof(int32_t) * nb);
+      if (nb > 0) std::memcpy(row, t->data(), sizeof(int32_t) * nb);   // an empty table has no data()
       for (int32_t j = nb; j < stride; ++j) row[j] = -1;
     }
     if (lens) lens[i] = len;
@@ -822,7 +822,7 @@ pa_status pa_bm_block_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32
   if (n_tokens) *n_tokens = len;
   if (out) {
     if (cap < nb) return fail(PA_ERR_INVALID, "cap smaller than the table");
-    std::memcpy(out, t->data(), sizeof(int32_t) * nb);
+    if (nb > 0) std::memcpy(out, t->data(), sizeof(int32_t) * nb);
   }
   return PA_OK;
 }
