@@ -6,7 +6,8 @@ attention layer of a model slice:
 1. the host block manager appends one token to each sequence
    (``pa_bm_step``: new block or copy-on-write pair, slot mapping, padded
    block tables and lengths, written into pinned host memory);
-2. the metadata goes to the device (async copies on the stream);
+2. the metadata goes to the device: one async copy, on a copy stream, into
+   one of two device arrays, so it overlaps the previous step's kernels;
 3. per layer: ``pa_copy_blocks`` (if the step made copy-on-write pairs),
    then one ``pa_decode_append`` call that writes the new token's K/V into
    its slot and attends over every cached token (``--separate-write``:
