@@ -21,9 +21,12 @@ the workload's shape, resident in HBM before timing starts.
 
 Printed: one JSON line.  ``value`` is KV bytes read by decode per second of
 the whole timed region (host step, copies and kernels included);
-``roofline`` is the decode call alone, timed with HIP events on its stream
-around one layer's call per timed step, the layer rotating (``--timed-layers
-all`` brackets every layer's; each event pair costs the step about 5 us);
+``roofline`` is the decode call alone, timed with HIP events on its stream.
+When each layer is one library call (``pa_decode_append``), one event pair
+brackets the layers' back-to-back calls of every fourth timed step and a call
+takes the span divided by the layers; otherwise a pair brackets one layer's
+call per step, the layer rotating (``--timed-layers``).  Each recorded pair
+leaves the GPU idle for about 5 us on either side;
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 workload on this host.
 
@@ -66,9 +69,12 @@ def parse_args():
                          "that many tokens")
     ap.add_argument("--decode", choices=["auto", "plain", "shared"], default="auto",
                     help="auto = pa_decode_shared_prefix when the batch has prefix groups, else pa_decode")
-    ap.add_argument("--timed-layers", choices=["one", "all"], default="one",
-                    help="decode calls bracketed by HIP events: one layer's per step, rotating (default), "
-                         "or every layer's")
+    ap.add_argument("--timed-layers", choices=["span", "one", "all"], default="span",
+                    help="decode calls bracketed by HIP events: span (default) = one pair around every layer's "
+                         "call of every --timed-every-th step, when each layer is one library call (else as "
+                         "'one'); one = one layer's call per step, rotating; all = every layer's call")
+    ap.add_argument("--timed-every", type=int, default=4,
+                    help="with --timed-layers span: the steps bracketed (every n-th)")
     ap.add_argument("--separate-write", action="store_true",
                     help="pa_write_kv then pa_decode per layer, instead of one pa_decode_append call (the KV write "
                          "inside the decode launch; the default wherever the batch has no prefix groups)")
@@ -242,15 +248,24 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
         stream.wait_event(hb.copied)
         ws = dev["workspace"]
         ws_bytes = ws.numel()
+        fused = fused_append and not shared_prefix
+        n_layers = len(st["pools"])
+        # "span": the layers' calls follow each other with nothing between
+        # (each is one pa_decode_append), so one event pair brackets them all
+        step_mode = None
+        if timing is not None:
+            if timing["mode"] == "span" and fused and not n_cow:
+                step_mode = "span" if (step0 + i) % timing["every"] == 0 else None
+            else:
+                step_mode = "all" if timing["mode"] == "all" else "one"
         for layer, pool in enumerate(st["pools"]):
             if n_cow:
                 check(L.pa_copy_blocks(pool.handle, meta["pairs"].data_ptr(), n_cow, sptr), "pa_copy_blocks")
-            fused = fused_append and not shared_prefix
             if not fused:
                 check(L.pa_write_kv(pool.handle, st["k_new"][layer].data_ptr(), st["v_new"][layer].data_ptr(),
                                     meta["slots"].data_ptr(), B, sptr), "pa_write_kv")
-            timed = timing is not None and (timing["all_layers"] or layer == (step0 + i) % len(st["pools"]))
-            if timed:
+            timed = step_mode == "all" or (step_mode == "one" and layer == (step0 + i) % n_layers)
+            if timed or (step_mode == "span" and layer == 0):
                 ev0, ev1 = timing["free"].pop()
                 ev0.record(stream)
             if shared_prefix:
@@ -272,7 +287,10 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
                                   sptr), "pa_decode")
             if timed:
                 ev1.record(stream)
-                timing["used"].append((ev0, ev1))
+                timing["used"].append((ev0, ev1, 1, i))
+            elif step_mode == "span" and layer == n_layers - 1:
+                ev1.record(stream)
+                timing["used"].append((ev0, ev1, n_layers, i))
         if meta["free"] is None:
             meta["free"] = torch.cuda.Event()
         meta["free"].record(stream)   # this step's kernels are the last readers of meta
@@ -647,10 +665,10 @@ def main():
                   max_len_override=max_ctx_bound)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    # HIP events around one layer's decode call per step, the layer rotating
-    # from step to step (or around every layer's): each recorded pair adds
-    # about 5 us of GPU time to a step
-    timing = {"used": [], "all_layers": args.timed_layers == "all",
+    # HIP events on the launch stream: each recorded pair leaves the GPU idle
+    # for about 5 us on either side, so by default one pair brackets the
+    # layers' back-to-back calls of every fourth step (--timed-layers)
+    timing = {"used": [], "mode": args.timed_layers, "every": max(1, args.timed_every),
               "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(args.steps * args.layers)]}
     torch.cuda.synchronize()
@@ -659,7 +677,8 @@ def main():
                          fused_append)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in timing["used"]]
+    spans = [(a.elapsed_time(b), n, i) for a, b, n, i in timing["used"]]   # (ms, calls bracketed, step)
+    dec_ms = [ms / n for ms, n, _ in spans]   # one call's duration per sample
     log(f"[bench] done: {elapsed * 1e3:.2f} ms for {args.steps} steps")
 
     total_kv = sum(b for b, _ in kv_bytes)
@@ -668,8 +687,15 @@ def main():
     # every layer's decode reads the same tokens (same tables and lengths);
     # the minimum traffic counts shared blocks once
     per_call_bytes = total_unique / (args.steps * layers)
-    mean_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
-    achieved = per_call_bytes / mean_dec_s / 1e9
+    # the bracketed calls' own bytes (lengths grow by one token per step) over their time
+    achieved = (sum(kv_bytes[i][1] / layers * n for _, n, i in spans) /
+                (sum(ms for ms, _, _ in spans) / 1e3) / 1e9)
+    mean_dec_s = sum(ms for ms, _, _ in spans) / sum(n for _, n, _ in spans) / 1e3
+    timing_note = (f"one HIP event pair around the {layers} layers' back-to-back decode calls of every "
+                   f"{timing['every']}th step ({len(spans)} spans), per call = span / {layers}"
+                   if all(n == layers for _, n, _ in spans) and layers > 1 else
+                   "one HIP event pair around each layer's decode call" if args.timed_layers == "all" else
+                   "one HIP event pair around one layer's decode call per step, the layer rotating")
     value = total_kv / elapsed / 1e9
     entry = "pa_decode_shared_prefix" if shared_prefix else ("pa_decode_append" if fused_append else "pa_decode")
     traffic, traffic_ratio = recorded_traffic(w.name, entry)
@@ -704,7 +730,8 @@ def main():
         "decode_call_us": {"mean": round(mean_dec_s * 1e6, 2),
                            "p10": round(dec_sorted[len(dec_sorted) // 10] * 1e3, 2),
                            "p50": round(dec_sorted[len(dec_sorted) // 2] * 1e3, 2),
-                           "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2)},
+                           "p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 2),
+                           "events": timing_note},
         "roofline": {
             "kernel": ("pa_decode_shared_prefix: decode_prefix_kernel + decode_partition_kernel" +
                        (" + decode_reduce_kernel" if resolved_part < max_ctx_bound else "") if shared_prefix else

@@ -113,12 +113,16 @@ def test_timed_steps_match_the_oracle(gpu, name, batch, decode, fused):
     history = []          # per step: oracle slots, pairs, tables, lens, ids, outputs of the checked layers
     for i in range(n_steps):
         timing = None
-        if i == n_steps - 1:   # the timed variant records HIP events around one layer's call
-            timing = {"used": [], "all_layers": False,
+        if i == n_steps - 1:   # the timed variant: HIP events around every layer's call (span), or one layer's
+            timing = {"used": [], "mode": "span", "every": 1,
                       "free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                                for _ in range(layers)]}
         bench.run_steps(pk, w, st, 1, run["part"], run["dev"], run["hbufs"], i, timing, run["shared_prefix"], fused)
         torch.cuda.synchronize()
+        if timing is not None:   # one span over both layers' calls when each is one pa_decode_append
+            spanned = fused and not run["shared_prefix"]
+            assert [n for _, _, n, _ in timing["used"]] == ([layers] if spanned else [1])
+            assert all(a.elapsed_time(b) > 0 for a, b, _, _ in timing["used"])
         # the oracle takes the same step
         order = ora.dispatch_order(ids)
         ids = [ids[k] for k in order]
