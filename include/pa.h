@@ -191,17 +191,18 @@ pa_status pa_swap_in(pa_pool* pool, const int32_t* blocks, int32_t n, const void
  *     valid block ids; block_table_stride ≥ ceil(max_context_len/block_size).
  *   context_lens: device int32[num_seqs], each in [0, max_context_len];
  *     a length of 0 gives a zero row.  Slots past the length are never used.
- *   max_context_len: host-known bound that sizes the launch.
+ *   max_context_len: host-known bound that sizes the launch, at most 2^30.
  *   scale: the logit scale; ≤ 0 selects 1/sqrt(head_dim).
  *   partition_tokens: how the context is split into work ([P2] §4.1's tiled
  *     softmax, merged with running max and sum):
  *       > 0 — fixed partitions of that many tokens (a multiple of
- *           block_size), merged by a second reduce kernel when a sequence
- *           has more than one.  Partitions of at most 512 tokens that hold
- *           whole chunks of the inner loop (16 tokens for 16-bit K/V with a
- *           group of ≥ 4 and blocks of ≥ 16 tokens; 8 to 32 on the vector
- *           loop) are taken one per wave, four consecutive ones to a
- *           workgroup, which merges them before it writes one partial result;
+ *           block_size, at most 2^30), merged by a second reduce kernel
+ *           when a sequence has more than one.  Partitions of at most 512
+ *           tokens that hold whole chunks of the inner loop (16 tokens for
+ *           16-bit K/V with a group of ≥ 4 and blocks of ≥ 16 tokens; 8 to
+ *           32 on the vector loop) are taken one per wave, four consecutive
+ *           ones to a workgroup, which merges them before it writes one
+ *           partial result;
  *           longer ones take one workgroup each;
  *       PA_PARTITION_UNIFORM — one grid of workgroups, all resident at
  *           once; the device picks the shortest partition length (a

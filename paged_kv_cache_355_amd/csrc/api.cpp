@@ -104,6 +104,18 @@ void layout_records(DecodePlan* plan, int64_t rows, int32_t head_dim) {
   plan->bytes = plan->o_off + rows * head_dim * 4;
 }
 
+// The kernels add a partition length to a partition's first token, and round
+// lengths up to whole blocks, in int32: the planners keep every token count
+// they accept at most 2^30.
+constexpr int32_t kMaxDecodeTokens = int32_t{1} << 30;
+
+pa_status check_token_counts(int32_t max_context_len, int32_t partition_tokens, int32_t max_prefix) {
+  if (max_context_len > kMaxDecodeTokens || max_prefix > kMaxDecodeTokens)
+    return fail(PA_ERR_INVALID, "max_context_len and max_prefix_tokens must be <= 2^30");
+  if (partition_tokens > kMaxDecodeTokens) return fail(PA_ERR_INVALID, "partition_tokens must be <= 2^30");
+  return PA_OK;
+}
+
 // How to split: an explicit positive partition length (a multiple of
 // block_size), PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM; for 0, the
 // PA_PARTITION_TOKENS override, else whole sequences (one workgroup per
@@ -114,6 +126,7 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
   const pa::PoolDesc& d = pool->d;
   if (requested < 0 && requested != PA_PARTITION_BALANCED && requested != PA_PARTITION_UNIFORM)
     return fail(PA_ERR_INVALID, "partition_tokens must be >= 0, PA_PARTITION_BALANCED or PA_PARTITION_UNIFORM");
+  if (pa_status s = check_token_counts(max_context_len, requested, 0)) return s;
   *plan = DecodePlan{};
   if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
     return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
@@ -121,6 +134,7 @@ pa_status plan_decode(const pa_pool* pool, int32_t num_seqs, int32_t q_heads, in
   const int32_t group = q_heads / d.kv_heads;
   const int64_t units = static_cast<int64_t>(num_seqs) * d.kv_heads;
   int32_t p = requested > 0 ? requested : (requested == 0 ? env_int("PA_PARTITION_TOKENS", 0) : 0);
+  if (pa_status s = check_token_counts(max_context_len, p, 0)) return s;
   pa::DecodeCapacity cap{};
   bool uniform = requested == PA_PARTITION_UNIFORM;
   if (p <= 0) {
@@ -190,6 +204,7 @@ pa_status plan_shared_prefix(const pa_pool* pool, int32_t num_seqs, int32_t q_he
                              int32_t max_prefix, int32_t requested, DecodePlan* plan) {
   const pa::PoolDesc& d = pool->d;
   if (requested < 0) return fail(PA_ERR_INVALID, "partition_tokens must be >= 0 for a shared-prefix decode");
+  if (pa_status s = check_token_counts(max_context_len, requested, max_prefix)) return s;
   if (q_heads % d.kv_heads != 0 || !pa::decode_supported(d.dtype, d.head_dim, d.block_size, q_heads / d.kv_heads))
     return fail(PA_ERR_UNSUPPORTED, "group size " + std::to_string(q_heads / d.kv_heads) +
                                         " (q_heads must be kv_heads x 1, 2, 4 or 8)");

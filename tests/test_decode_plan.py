@@ -175,3 +175,26 @@ def test_shared_prefix_without_a_prefix_sizes_like_pa_decode():
                                                            ctypes.byref(nbytes))
         assert rc == PA_OK
         assert nbytes.value == plan(pool, 8, 4, 2000, 64)[3]
+
+
+@pytest.mark.parametrize("max_ctx,p", [((1 << 30) + 1, 512), (4096, (1 << 30) + 16), ((1 << 31) - 1, 16)])
+def test_token_counts_above_2_30_are_rejected(max_ctx, p):
+    """The kernels add a partition length to a partition's first token in
+    int32: lengths and partition lengths above 2^30 are refused."""
+    pool = HostPool(64, 16, 2, 128, "f16")
+    rc1, rc2, _, _ = plan(pool, 4, 4, max_ctx, p)
+    assert rc1 == PA_ERR_INVALID and rc2 == PA_ERR_INVALID
+
+
+def test_token_counts_of_2_30_are_accepted():
+    pool = HostPool(64, 16, 2, 128, "f16")
+    assert plan(pool, 4, 4, 1 << 30, 1 << 30) == (PA_OK, PA_OK, 1 << 30, 0)
+
+
+def test_shared_prefix_token_counts_above_2_30_are_rejected():
+    pool = HostPool(64, 16, 32, 128, "f16")
+    nbytes = ctypes.c_int64()
+    for max_ctx, max_prefix, p in [(4096, (1 << 30) + 16, 64), ((1 << 30) + 1, 512, 64), (4096, 512, (1 << 30) + 16)]:
+        rc = lib().pa_decode_shared_prefix_workspace_bytes(pool.handle, 8, 32, max_ctx, max_prefix, p,
+                                                           ctypes.byref(nbytes))
+        assert rc == PA_ERR_INVALID, (max_ctx, max_prefix, p)
