@@ -47,6 +47,9 @@
 //   * Fixed partitions (an explicit partition length): one workgroup per
 //     (sequence, kv-head, partition of P tokens) and a second kernel,
 //     decode_reduce_kernel, merges the partitions of longer sequences.
+//     Partitions of at most 512 tokens that hold whole chunks are taken one
+//     per wave, NW consecutive ones to a workgroup, which merges them in LDS
+//     before it writes one record (wave_tokens).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -571,6 +574,8 @@ __device__ __forceinline__ void attend_range_mfma(const char* __restrict__ k_poo
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
+    // This wave's run of chunks, as in the vector loop: two per iteration
+    // through two named buffers, the next chunk's loads in flight.
     uint4 ka[NKL], va[NKL], kb2[NKL], vb2[NKL];
     const ChunkDeal dl = deal_chunks<CT, NW>(wave, wave_tokens, t_begin, t_end, tb, te);
     const int32_t lim = dl.limit;
@@ -818,10 +823,12 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ k_pool, co
       }
     };
 
-    // Chunks wave, wave+NW, wave+2NW, … with the next chunk's loads in flight.
-    // (The scheduling barriers keep the compiler from hoisting the current
-    // chunk's arithmetic above the next chunk's load issue, which would make
-    // the wave wait for its data before the prefetch leaves.)
+    // This wave's run of chunks [first, limit) (deal_chunks), two per
+    // iteration through two named buffers, with the next chunk's loads in
+    // flight while the current one is consumed.  (The scheduling barriers keep
+    // the compiler from hoisting the current chunk's arithmetic above the next
+    // chunk's load issue, which would make the wave wait for its data before
+    // the prefetch leaves.)
     uint4 ka[NLC], va[NLC], kb2[NLC], vb2[NLC];
     const ChunkDeal dl = deal_chunks<CT, NW>(wave, wave_tokens, t_begin, t_end, tb, te);
     const int32_t lim = dl.limit;
