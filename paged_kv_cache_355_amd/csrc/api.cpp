@@ -372,9 +372,9 @@ pa_status pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int32_t n, void* s
       const int32_t a = h[2 * i], b = h[2 * i + 1];
       if (a < 0 || a >= pool->d.num_blocks || b < 0 || b >= pool->d.num_blocks)
         return fail(PA_ERR_INVALID, "copy pair outside the pool");
-      if (role[a] == 2) return fail(PA_ERR_INVALID, "a source block is also a destination");
       role[a] = 1;
     }
+    // every destination once, and never a block that any pair reads
     for (int32_t i = 0; i < n; ++i) {
       const int32_t b = h[2 * i + 1];
       if (role[b] != 0) return fail(PA_ERR_INVALID, "destination block repeats or is a source");

@@ -108,6 +108,34 @@ def test_copy_then_write_follows_stream_order(gpu):
     assert np.array_equal(to_bits(pool.k, "f16"), k_want) and np.array_equal(to_bits(pool.v, "f16"), v_want)
 
 
+def test_write_and_copy_refuse_aliasing_under_validation(gpu):
+    """PA_DEBUG_VALIDATE turns the race contracts of the write and the copy
+    into errors before anything is launched: a slot written twice or outside
+    the pool; a destination block that repeats, that another pair reads, or a
+    pair outside the pool.  The pool is unchanged after every refusal."""
+    import torch
+    pk = gpu
+    rng = np.random.default_rng(23)
+    nb, bs, kvh, d = 8, 4, 2, 64
+    k0, v0 = draw(rng, (nb, kvh, bs, d), "f16", 1.0), draw(rng, (nb, kvh, bs, d), "f16", 1.0)
+    pool = pk.Pool(nb, bs, kvh, d, "f16", k=to_torch(k0, "f16"), v=to_torch(v0, "f16"))
+    kn, vn = to_torch(draw(rng, (3, kvh, d), "f16", 1.0), "f16"), to_torch(draw(rng, (3, kvh, d), "f16", 1.0), "f16")
+    for slots, why in [([5, 9, 5], "written twice"), ([5, 9, nb * bs], "outside the pool")]:
+        with pytest.raises(pk.PaError) as e:
+            pk.write_kv(pool, kn, vn, torch.tensor(slots, dtype=torch.int32).cuda())
+        assert e.value.code == -1 and why in str(e.value), slots
+    for pairs in ([[1, 2], [3, 2]],      # a destination twice
+                  [[1, 2], [2, 3]],      # a destination that the next pair reads
+                  [[4, 1], [1, 2]],      # a source that an earlier pair writes
+                  [[1, 2], [3, 3]],      # a block copied onto itself
+                  [[1, nb]]):            # outside the pool
+        with pytest.raises(pk.PaError) as e:
+            pk.copy_blocks(pool, torch.tensor(pairs, dtype=torch.int32).cuda())
+        assert e.value.code == -1, pairs
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(pool.k, "f16"), k0) and np.array_equal(to_bits(pool.v, "f16"), v0)
+
+
 # ----------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------
