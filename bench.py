@@ -255,7 +255,8 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
         step_mode = None
         if timing is not None:
             if timing["mode"] == "span" and fused and not n_cow:
-                step_mode = "span" if (step0 + i) % timing["every"] == 0 else None
+                # counted from this call's first step, so any run brackets at least one
+                step_mode = "span" if i % timing["every"] == 0 else None
             else:
                 step_mode = "all" if timing["mode"] == "all" else "one"
         for layer, pool in enumerate(st["pools"]):

@@ -55,6 +55,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <type_traits>
@@ -1818,13 +1819,14 @@ __global__ __launch_bounds__(NW * 64, (kMinWavesExtra<DT, BS, G, true>)) void de
 // ---------------------------------------------------------------------------
 
 // Workgroups of `kernel` (kThreads threads, static LDS only) that the current
-// device holds at once; cached per device in `cache`.
+// device holds at once; cached per device in `cache` (atomics: host threads
+// may ask at once, and all compute the same value).
 template <typename Kernel>
-hipError_t resident_workgroups(Kernel kernel, int (&cache)[64], int32_t* resident_out) {
+hipError_t resident_workgroups(Kernel kernel, std::atomic<int> (&cache)[64], int32_t* resident_out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int resident = dev >= 0 && dev < 64 ? cache[dev] : 0;
+  int resident = dev >= 0 && dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (resident == 0) {
     int per_cu = 0, cus = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
@@ -1833,7 +1835,7 @@ hipError_t resident_workgroups(Kernel kernel, int (&cache)[64], int32_t* residen
     if (e != hipSuccess) return e;
     resident = per_cu * cus;
     if (resident <= 0) resident = cus > 0 ? cus : 1;
-    if (dev >= 0 && dev < 64) cache[dev] = resident;
+    if (dev >= 0 && dev < 64) cache[dev].store(resident, std::memory_order_relaxed);
   }
   *resident_out = resident;
   return hipSuccess;
@@ -1844,7 +1846,7 @@ hipError_t resident_workgroups(Kernel kernel, int (&cache)[64], int32_t* residen
 template <int DT, int D, int BS, int G>
 hipError_t balanced_grid(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, int32_t* grid) {
   constexpr int CT = Chunk<DT, D, BS>::CT;
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int32_t resident = 0;
   hipError_t e = resident_workgroups(decode_balanced_kernel<DT, D, BS, G, kWaves>, cache, &resident);
   if (e != hipSuccess) return e;
@@ -1987,7 +1989,7 @@ struct LaunchFn {
 template <int DT, int D, int BS, int G>
 struct CapacityFn {
   static hipError_t run(const PoolDesc& p, int32_t num_seqs, int32_t max_ctx, DecodeCapacity* cap) {
-    static int partition_cache[64], uniform_cache[64];
+    static std::atomic<int> partition_cache[64], uniform_cache[64];
     hipError_t e = balanced_grid<DT, D, BS, G>(p, num_seqs, max_ctx, &cap->balanced_grid);
     if (e != hipSuccess) return e;
     e = resident_workgroups(decode_partition_kernel<DT, D, BS, G, kWaves, false>, partition_cache, &cap->partition);
