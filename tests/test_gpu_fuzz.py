@@ -22,7 +22,7 @@ from tests.gpu_util import build_case, to_torch, to_bits, out_to_f64, NAN_BITS, 
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 200
 OUT_HALF_ULP = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}   # relative, round to nearest
 
 
@@ -106,7 +106,7 @@ def test_random_case_matches_oracle(gpu, i):
             assert np.all(got[s] == 0.0)
 
 
-N_FAMILY_CASES = 24
+N_FAMILY_CASES = 64
 
 
 def draw_families(i):
