@@ -20,6 +20,7 @@ import ctypes
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 from paged_kv_cache_355_amd._lib import lib
 
@@ -198,3 +199,19 @@ def test_shared_prefix_token_counts_above_2_30_are_rejected():
         rc = lib().pa_decode_shared_prefix_workspace_bytes(pool.handle, 8, 32, max_ctx, max_prefix, p,
                                                            ctypes.byref(nbytes))
         assert rc == PA_ERR_INVALID, (max_ctx, max_prefix, p)
+
+
+@settings(max_examples=400, deadline=None)
+@given(dtype=st.sampled_from(sorted(DTYPES)), head_dim=st.sampled_from([64, 128]),
+       block_size=st.sampled_from([4, 8, 16, 32, 64]), kv_heads=st.integers(1, 8),
+       group=st.sampled_from([1, 2, 4, 8]), num_seqs=st.integers(1, 300), max_ctx=st.integers(0, 200000),
+       blocks=st.integers(1, 300))
+def test_fixed_partition_plan_for_any_sizes(dtype, head_dim, block_size, kv_heads, group, num_seqs, max_ctx,
+                                            blocks):
+    """The documented layout for random pool shapes, groups, batch sizes,
+    lengths and partition lengths (a whole number of blocks)."""
+    pool = HostPool(4, block_size, kv_heads, head_dim, dtype)
+    q_heads = kv_heads * group
+    p = blocks * block_size
+    assert plan(pool, num_seqs, q_heads, max_ctx, p) == (PA_OK, PA_OK, *expected_plan(pool, num_seqs, q_heads,
+                                                                                         max_ctx, p))
