@@ -200,6 +200,20 @@ def prepare_run(pk, w, st, partition_arg=0, decode_arg="auto"):
 # ----------------------------------------------------------------------------
 # the timed step
 # ----------------------------------------------------------------------------
+def step_timing(timing, fused, n_cow, i):
+    """How step i of a run_steps call is bracketed by HIP events: "span" (one
+    pair around every layer's call), "one" (one layer's call, rotating), "all"
+    (every layer's call) or None.  Span mode applies when each layer is one
+    library call (pa_decode_append, no copy-on-write copies before it) and
+    takes every timing["every"]-th step counted from the call's first, so any
+    run brackets at least one; otherwise it falls back to "one"."""
+    if timing is None:
+        return None
+    if timing["mode"] == "span" and fused and not n_cow:
+        return "span" if i % timing["every"] == 0 else None
+    return "all" if timing["mode"] == "all" else "one"
+
+
 def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, shared_prefix, fused_append,
               max_len_override=None):
     """n_steps decode steps; returns per-step KV bytes read by decode.  With
@@ -250,15 +264,7 @@ def run_steps(pk, w, st, n_steps, partition_tokens, dev, hbufs, step0, timing, s
         ws_bytes = ws.numel()
         fused = fused_append and not shared_prefix
         n_layers = len(st["pools"])
-        # "span": the layers' calls follow each other with nothing between
-        # (each is one pa_decode_append), so one event pair brackets them all
-        step_mode = None
-        if timing is not None:
-            if timing["mode"] == "span" and fused and not n_cow:
-                # counted from this call's first step, so any run brackets at least one
-                step_mode = "span" if i % timing["every"] == 0 else None
-            else:
-                step_mode = "all" if timing["mode"] == "all" else "one"
+        step_mode = step_timing(timing, fused, n_cow, i)
         for layer, pool in enumerate(st["pools"]):
             if n_cow:
                 check(L.pa_copy_blocks(pool.handle, meta["pairs"].data_ptr(), n_cow, sptr), "pa_copy_blocks")

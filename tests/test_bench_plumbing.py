@@ -58,3 +58,20 @@ def test_recorded_traffic_summaries_are_consistent(workload):
         assert got == (rec["hbm_bytes_per_call"], round(ratio, 4))
     else:
         assert got == (None, None)
+
+
+def test_span_timing_brackets_at_least_one_step_of_any_run():
+    """Span timing takes every n-th step counted from the run's first, so a
+    short run (a 3-step counter pass) still records one span; steps with other
+    kernels between the layers' calls fall back to one rotating layer."""
+    import bench
+    span = {"mode": "span", "every": 4}
+    for steps in (1, 3, 4, 5, 50):
+        modes = [bench.step_timing(span, True, 0, i) for i in range(steps)]
+        assert modes.count("span") == -(-steps // 4) and modes[0] == "span"
+        assert set(modes) <= {"span", None}
+    assert bench.step_timing(span, False, 0, 0) == "one"          # pa_write_kv between the calls
+    assert bench.step_timing(span, True, 3, 0) == "one"           # copy-on-write copies first
+    assert bench.step_timing({"mode": "all", "every": 4}, True, 0, 1) == "all"
+    assert bench.step_timing({"mode": "one", "every": 4}, True, 0, 1) == "one"
+    assert bench.step_timing(None, True, 0, 0) is None
