@@ -55,6 +55,8 @@ class Pool:
         self.kv_heads, self.head_dim, self.dtype = int(kv_heads), int(head_dim), dtype
         shape = (self.num_blocks, self.kv_heads, self.block_size, self.head_dim)
         tdt = torch_dtype(dtype)
+        if (k is None) != (v is None):
+            raise ValueError("pass both k and v (caller memory) or neither (allocated here)")
         if k is None:
             device = device or "cuda"
             k = torch.empty(shape, dtype=tdt, device=device)

@@ -62,3 +62,16 @@ def test_errors_are_reported_without_a_gpu():
     with pytest.raises(pk.PaError) as e:
         bm.free_seq(7)
     assert e.value.code == -5
+
+
+def test_pool_takes_both_tensors_or_neither():
+    """Caller memory means both K and V; the binding says so before any device work."""
+    import torch
+    import paged_kv_cache_355_amd as pk
+    k = torch.empty((4, 1, 16, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="both k and v"):
+        pk.Pool(4, 16, 1, 64, "f16", k=k)
+    with pytest.raises(ValueError, match="both k and v"):
+        pk.Pool(4, 16, 1, 64, "f16", v=k)
+    with pytest.raises(ValueError, match="device tensor"):          # host tensors are refused too
+        pk.Pool(4, 16, 1, 64, "f16", k=k, v=k.clone())
